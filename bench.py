@@ -1,0 +1,214 @@
+"""Throughput of one Qwen3 decoder layer, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+q3l_layer_forward (saving intermediates) then q3l_layer_backward (dx and all
+eleven fp32 weight gradients), on the Qwen3-8B-shaped layer (d=4096, 32 q /
+8 kv heads, d_h=128, d_ffn=12288, B=2, L=4096, bf16).  Inputs and weights
+are resident in HBM before the timed region.  Rank 0 prints one JSON line.
+
+Besides the step timing it measures, with HIP events on the stream the
+library launches on, the dominant kernel (the fused gate/up GEMM with the
+SwiGLU epilogue, launched through its phase-level entry point with the
+layer's shapes), and times the fp64 CPU oracle on a bounded sample of the
+same workload as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = ("decoder-layer fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), "
+          "1 MI355X")
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "qwen3-8b-bf16-fwd-bwd": 4,
+    "qwen3-8b-bf16-fwd": 2,
+    "llama70b-tp8-share-bf16-fwd": 3,
+    "tiny-dims-bf16-fwd-L2048": 1,
+}
+
+
+def model_flops(c: dict, backward: bool) -> dict:
+    """Model FLOPs of one layer pass (attention counts causal pairs)."""
+    T, d, f = c["B"] * c["L"], c["d"], c["d_ffn"]
+    qd, kvd = c["h_q"] * c["d_h"], c["h_kv"] * c["d_h"]
+    gemm = 2 * T * d * (qd + 2 * kvd) + 2 * T * qd * d + 2 * T * d * 2 * f \
+        + 2 * T * f * d
+    pairs = c["B"] * c["L"] * (c["L"] + 1) // 2
+    attn = 4 * c["h_q"] * c["d_h"] * pairs
+    out = {"gemm_fwd": gemm, "attn_fwd": attn}
+    total = gemm + attn
+    if backward:
+        total += 2 * gemm + 2 * attn
+        out["attn_recompute"] = 2 * c["h_q"] * c["d_h"] * pairs
+    out["total"] = total
+    return out
+
+
+def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
+    import torch
+    import qwen3_decoder_layer_amd as q3
+    lc = q3.LayerConfig.from_dict(cfg)
+    bf = torch.bfloat16
+    dev = "cuda"
+
+    def up(a):
+        return torch.from_numpy(a).to(device=dev, dtype=bf)
+
+    W = {n: up(inp[n]) for n in synth.PARAM_NAMES}
+    x = up(inp["x"])
+    backward = cfg["backward"]
+    saved = torch.empty(q3.saved_bytes(lc), dtype=torch.uint8, device=dev)
+    out = {}
+    if cfg.get("tp_partial"):
+        out = {k: torch.empty((lc.B, lc.L, lc.d), dtype=torch.float32, device=dev)
+               for k in ("attn_partial", "mlp_partial")}
+    else:
+        out = {"y": torch.empty_like(x)}
+    if backward:
+        dy = up(inp["dy"])
+        dx = torch.empty_like(x)
+        grads = {n: torch.empty(W[n].shape, dtype=torch.float32, device=dev)
+                 for n in synth.PARAM_NAMES}
+        ws = torch.empty(q3.workspace_bytes(lc, True), dtype=torch.uint8,
+                         device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        q3.layer_forward(lc, W, x, out=out, saved=saved, stream=stream)
+        if backward:
+            q3.layer_backward(lc, W, x, dy, saved, dx=dx, grads=grads,
+                              workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Dominant kernel: the fused gate/up + SwiGLU GEMM, same shapes as in the
+    # layer, timed with HIP events on the launch stream.
+    T = lc.T
+    hn = torch.randn((T, lc.d), device=dev).to(bf)
+    f = torch.empty((T, lc.d_ffn), dtype=bf, device=dev)
+    gu = torch.empty((T, 2 * lc.d_ffn), dtype=bf, device=dev)
+    reps = max(10, steps)
+    for _ in range(3):
+        q3.swiglu_fwd(hn, W["gate"], W["up"], f=f, gu=gu, stream=stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        q3.swiglu_fwd(hn, W["gate"], W["up"], f=f, gu=gu, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = ev0.elapsed_time(ev1) / reps
+    del saved
+    return {"elapsed": elapsed, "kernel_ms": k_ms,
+            "kernel_flops": 2.0 * T * lc.d * 2 * lc.d_ffn}
+
+
+def cpu_baseline(cfg: dict, budget_tokens: int) -> dict:
+    """The fp64 oracle, untuned, on one sequence of `budget_tokens` tokens of
+    the same layer (forward + backward when the workload has a backward)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    c = dict(cfg, B=1, L=budget_tokens)
+    inp = synth.make_inputs(c, 1000 + 4, with_dy=cfg["backward"])
+    p = {n: inp[n] for n in synth.PARAM_NAMES}
+    t0 = time.perf_counter()
+    if cfg["backward"]:
+        oracle.layer_backward(c, p, inp["x"], inp["dy"])   # runs the forward too
+    else:
+        oracle.layer_forward(c, p, inp["x"])
+    dt = time.perf_counter() - t0
+    return {"value": budget_tokens / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"1 sequence x {budget_tokens} tokens of the same layer "
+                       f"(d={cfg['d']}, {cfg['h_q']}/{cfg['h_kv']} heads, "
+                       f"d_ffn={cfg['d_ffn']}), numpy fp64, "
+                       f"{'fwd+bwd' if cfg['backward'] else 'fwd'}, "
+                       f"{dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3-8b-bf16-fwd-bwd",
+                    choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the layer's local compute runs on a single device).",
+              file=sys.stderr)
+        sys.exit(2)
+    cfg, inp = synth.preset_inputs(WORKLOADS[args.workload])
+    res = gpu_run(cfg, inp, args.steps, args.warmup)
+    fl = model_flops(cfg, cfg["backward"])
+    T = cfg["B"] * cfg["L"]
+    ms = res["elapsed"] / args.steps * 1e3
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    k_tflops = res["kernel_flops"] / (res["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: x, dy ~ N(0,1); projections ~ N(0,0.02); "
+                "norm weights ~ 1+N(0,0.1); rounded to bf16)",
+        "config": {"workload": cfg["name"], "d": cfg["d"], "h_q": cfg["h_q"],
+                   "h_kv": cfg["h_kv"], "d_h": cfg["d_h"], "d_ffn": cfg["d_ffn"],
+                   "B": cfg["B"], "L": cfg["L"], "tokens": T,
+                   "pass": "fwd+bwd" if cfg["backward"] else "fwd",
+                   "parallelism": "none (1 GPU)"},
+        "tflops": tflops,
+        "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "model_flops_per_step": fl["total"],
+        "roofline": {"kernel": "gate/up GEMM + SwiGLU epilogue "
+                               f"[{T}x{cfg['d']}] x [{2 * cfg['d_ffn']}x{cfg['d']}]^T",
+                     "bound": "mfma", "achieved": k_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": k_tflops / PEAK_BF16_TFLOPS,
+                     "avg_ms": res["kernel_ms"], "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

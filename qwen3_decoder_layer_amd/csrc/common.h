@@ -1,0 +1,103 @@
+// Shared device-side helpers for the gfx950 kernels: bf16 conversion, vector
+// types, MFMA wrappers, wave reductions and the in-register 8x8 transpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3l {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+__host__ __device__ inline float bf2f(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest, ties to even (inputs are finite).
+__host__ __device__ inline bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+__host__ __device__ inline uint32_t pack2(float lo, float hi) {
+  return static_cast<uint32_t>(f2bf(lo)) |
+         (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+__host__ __device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__host__ __device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---- generic element access for the fp32 / bf16 kernels --------------------
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static inline float load(const float* p) { return *p; }
+  __device__ static inline void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static inline float load(const bf16_t* p) { return bf2f(*p); }
+  __device__ static inline void store(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// ---- 16-byte global / LDS moves -------------------------------------------
+__device__ inline u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ inline void st16(void* p, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+__device__ inline u32x2_t ld8(const void* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+__device__ inline void st8(void* p, u32x2_t v) {
+  *reinterpret_cast<u32x2_t*>(p) = v;
+}
+
+// ---- 8x8 transpose of 16-bit elements held as 8 rows of 4 dwords ----------
+// in[r] holds elements (r, 0..7) (two per dword, low half first); out[c]
+// receives elements (0..7, c).
+__host__ __device__ inline void transpose8x8(const u32x4_t in[8], u32x4_t out[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = in[2 * j][c >> 1];
+      const uint32_t b = in[2 * j + 1][c >> 1];
+      out[c][j] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
+                          : ((a & 0xFFFFu) | (b << 16));
+    }
+  }
+}
+
+// ---- MFMA wrappers ---------------------------------------------------------
+// mfma32(a, b, c): D[r][col] += sum_k A[r][k] B[k][col] for a 32x32x16 bf16
+// tile.  Lane l supplies A[l%32][8*(l/32)+j] in a[j] and B[8*(l/32)+j][l%32]
+// in b[j]; it receives D[8*(i/4) + 4*(l/32) + i%4][l%32] in d[i].
+__device__ inline f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b,
+                                  const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
+
+// ---- wave reductions (wave64) ---------------------------------------------
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ inline float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
+  return (a + b - 1) / b;
+}
+
+}  // namespace q3l

@@ -1,0 +1,468 @@
+// Norm-family kernels of the Qwen3 decoder layer: RMSNorm forward/backward
+// (walkthrough page, Steps 1 and 8), the per-head q_norm/k_norm fused with
+// RoPE (Steps 3-4) and its backward, the RoPE angle table, and the column
+// reduction of per-block weight-gradient partials.
+//
+// All of these are HBM-bound: each reads its inputs once and writes its
+// outputs once with 16-byte accesses; reductions over a row stay inside a
+// wave64 (shuffles), reductions over rows go through per-block partial sums.
+#include "common.h"
+#include "ops.h"
+
+namespace q3l {
+namespace {
+
+// Eight consecutive elements as fp32 (one 16-byte access for bf16, two for
+// fp32).
+template <class T> struct V8;
+template <> struct V8<bf16_t> {
+  __device__ static void load(const bf16_t* p, float f[8]) {
+    const u32x4_t v = ld16(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[2 * j] = lo_f(v[j]); f[2 * j + 1] = hi_f(v[j]); }
+  }
+  __device__ static void store(bf16_t* p, const float f[8]) {
+    st16(p, u32x4_t{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]),
+                    pack2(f[6], f[7])});
+  }
+};
+template <> struct V8<float> {
+  __device__ static void load(const float* p, float f[8]) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[j] = a[j]; f[4 + j] = b[j]; }
+  }
+  __device__ static void store(float* p, const float f[8]) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{f[4], f[5], f[6], f[7]};
+  }
+};
+
+// ---- RMSNorm forward: one wave per row ------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(
+    int64_t rows, int n, const T* __restrict__ x, const T* __restrict__ w,
+    float eps, T* __restrict__ y, float* __restrict__ rstd) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + row * n;
+  T* yr = y + row * n;
+  const int nc = n / 8;
+  float ss = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    float f[8];
+    V8<T>::load(xr + 8 * c, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)n + eps);
+  for (int c = lane; c < nc; c += 64) {
+    float f[8], g[8];
+    V8<T>::load(xr + 8 * c, f);
+    V8<T>::load(w + 8 * c, g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = f[j] * r * g[j];
+    V8<T>::store(yr + 8 * c, f);
+  }
+  if (lane == 0) rstd[row] = r;
+}
+
+// ---- RMSNorm backward -----------------------------------------------------
+// Per row r (xhat = x * rstd, g = dy * w):
+//   dx = rstd * (g - xhat * mean(g * xhat)) + resid
+// and the block accumulates dw = sum_rows dy * xhat into one partial row.
+// CPL = 8-element chunks per lane (n <= 512 * CPL).
+template <class T, int CPL>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
+    int64_t rows, int n, const T* __restrict__ dy, const T* __restrict__ x,
+    const float* __restrict__ rstd, const T* __restrict__ w,
+    const void* __restrict__ resid, int resid_f32, T* __restrict__ dx,
+    float* __restrict__ dx32, float* __restrict__ wpart) {
+  extern __shared__ float sdw[];  // [n]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nc = n / 8;
+  for (int i = threadIdx.x; i < n; i += 256) sdw[i] = 0.f;
+  float acc[CPL][8];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
+  __syncthreads();
+
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += nwaves) {
+    const float r = rstd[row];
+    const T* dyr = dy + row * n;
+    const T* xr = x + row * n;
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        float a[8], b[8], ww[8];
+        V8<T>::load(dyr + 8 * ch, a);
+        V8<T>::load(xr + 8 * ch, b);
+        V8<T>::load(w + 8 * ch, ww);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float xh = b[j] * r;
+          dot += a[j] * ww[j] * xh;
+          acc[c][j] += a[j] * xh;
+        }
+      }
+    }
+    dot = wave_sum(dot) / (float)n;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        float a[8], b[8], ww[8], o[8];
+        V8<T>::load(dyr + 8 * ch, a);
+        V8<T>::load(xr + 8 * ch, b);
+        V8<T>::load(w + 8 * ch, ww);
+        float rr[8];
+        if (resid_f32) {
+          V8<float>::load(static_cast<const float*>(resid) + row * n + 8 * ch, rr);
+        } else if (resid) {
+          V8<T>::load(static_cast<const T*>(resid) + row * n + 8 * ch, rr);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rr[j] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          o[j] = r * (a[j] * ww[j] - b[j] * r * dot) + rr[j];
+        if (dx) V8<T>::store(dx + row * n + 8 * ch, o);
+        if (dx32) V8<float>::store(dx32 + row * n + 8 * ch, o);
+      }
+    }
+  }
+  // Waves add their partials one after another: a fixed summation order, so
+  // the weight gradient is bitwise reproducible.
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nc)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sdw[8 * ch + j] += acc[c][j];
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < n; i += 256) wpart[(int64_t)blockIdx.x * n + i] = sdw[i];
+}
+
+constexpr int kNormBwdParts = 256;
+
+// ---- column reduction of partial rows -------------------------------------
+__global__ __launch_bounds__(256) void reduce_rows_kernel(
+    const float* __restrict__ part, int nparts, int n, float* __restrict__ out,
+    int accumulate) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * n + i];
+  out[i] = accumulate ? out[i] + s : s;
+}
+
+// ---- RoPE angle table: angle(t, i) = t * theta^(-2i/d_h), in double --------
+__global__ void rope_table_kernel(int L, int d_h, double theta,
+                                  float* __restrict__ cos_t,
+                                  float* __restrict__ sin_t) {
+  const int half = d_h / 2;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= L * half) return;
+  const int t = idx / half, i = idx % half;
+  const double inv = pow(theta, -2.0 * (double)i / (double)d_h);
+  const double a = (double)t * inv;
+  cos_t[idx] = (float)cos(a);
+  sin_t[idx] = (float)sin(a);
+}
+
+// ---- q/k norm + RoPE forward ----------------------------------------------
+// One group of LP = d_h/8 lanes per (token, head) vector; lane j holds
+// elements 8j..8j+7.  Rotate-half pairing: element i (< d_h/2) pairs with
+// i + d_h/2, which sits in lane j ^ (LP/2).
+template <class T, int DH>
+__global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
+    int64_t tokens, int L, int h_q, int h_kv, int qk_norm, float eps,
+    const T* __restrict__ in, int64_t ld_in, const T* __restrict__ wq,
+    const T* __restrict__ wk, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, T* __restrict__ out, int64_t ld_out,
+    float* __restrict__ rstd_q, float* __restrict__ rstd_k) {
+  constexpr int LP = DH / 8, HALF = LP / 2;
+  const int lane = threadIdx.x & 63;
+  const int j = lane % LP;
+  const int heads = h_q + h_kv;
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
+  const bool valid = item < tokens * heads;
+  const int64_t it = valid ? item : 0;
+  const int64_t t = it / heads;
+  const int hh = (int)(it % heads);
+  const int pos = (int)(t % L);
+  const bool isq = hh < h_q;
+  float v[8], wv[8];
+  V8<T>::load(in + t * ld_in + (int64_t)hh * DH + 8 * j, v);
+  float r = 1.f;
+  if (qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    ss = group_sum(ss, LP);
+    r = 1.0f / sqrtf(ss / (float)DH + eps);
+    V8<T>::load((isq ? wq : wk) + 8 * j, wv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * r * wv[e];
+  }
+  float pv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pv[e] = __shfl_xor(v[e], HALF, 64);
+  const int i0 = 8 * (j % HALF);
+  const float* cr = cos_t + (int64_t)pos * (DH / 2) + i0;
+  const float* sr = sin_t + (int64_t)pos * (DH / 2) + i0;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = cr[e], s = sr[e];
+    o[e] = (j < HALF) ? v[e] * c - pv[e] * s : v[e] * c + pv[e] * s;
+  }
+  if (!valid) return;
+  V8<T>::store(out + t * ld_out + (int64_t)hh * DH + 8 * j, o);
+  if (qk_norm && j == 0) {
+    if (isq) rstd_q[t * h_q + hh] = r;
+    else rstd_k[t * h_kv + (hh - h_q)] = r;
+  }
+}
+
+// ---- q/k norm + RoPE backward ---------------------------------------------
+// g: gradient w.r.t. the rotated, normalised q/k.  Inverse rotation, then the
+// RMSNorm adjoint per head; dw_q / dw_k partial sums per block.
+template <class T, int DH>
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
+    int64_t tokens, int L, int h_q, int h_kv, int qk_norm,
+    const T* __restrict__ g, int64_t ld_g, const T* __restrict__ pre,
+    int64_t ld_pre, const T* __restrict__ wq, const T* __restrict__ wk,
+    const float* __restrict__ rstd_q, const float* __restrict__ rstd_k,
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+    T* __restrict__ out, int64_t ld_out, float* __restrict__ wq_part,
+    float* __restrict__ wk_part) {
+  constexpr int LP = DH / 8, HALF = LP / 2;
+  __shared__ float sq[DH], sk[DH];
+  const int lane = threadIdx.x & 63;
+  const int j = lane % LP;
+  const int heads = h_q + h_kv;
+  for (int i = threadIdx.x; i < DH; i += 256) { sq[i] = 0.f; sk[i] = 0.f; }
+  __syncthreads();
+  float aq[8], ak[8], wqv[8], wkv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { aq[e] = 0.f; ak[e] = 0.f; }
+  if (qk_norm) {
+    V8<T>::load(wq + 8 * j, wqv);
+    V8<T>::load(wk + 8 * j, wkv);
+  }
+  const int64_t total = tokens * heads;
+  const int64_t stride = (int64_t)gridDim.x * (256 / LP);
+  const int64_t first = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
+  const int64_t niter = (total + stride - 1) / stride;
+  for (int64_t k = 0; k < niter; ++k) {
+    const int64_t item = first + k * stride;
+    const bool valid = item < total;
+    const int64_t it = valid ? item : 0;
+    const int64_t t = it / heads;
+    const int hh = (int)(it % heads);
+    const int pos = (int)(t % L);
+    const bool isq = hh < h_q;
+    float gv[8], pg[8];
+    V8<T>::load(g + t * ld_g + (int64_t)hh * DH + 8 * j, gv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pg[e] = __shfl_xor(gv[e], HALF, 64);
+    const int i0 = 8 * (j % HALF);
+    const float* cr = cos_t + (int64_t)pos * (DH / 2) + i0;
+    const float* sr = sin_t + (int64_t)pos * (DH / 2) + i0;
+    float dn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = cr[e], s = sr[e];
+      dn[e] = (j < HALF) ? gv[e] * c + pg[e] * s : gv[e] * c - pg[e] * s;
+    }
+    float o[8];
+    if (qk_norm) {
+      float xv[8];
+      V8<T>::load(pre + t * ld_pre + (int64_t)hh * DH + 8 * j, xv);
+      const float r = isq ? rstd_q[t * h_q + hh] : rstd_k[t * h_kv + (hh - h_q)];
+      const float* wv = isq ? wqv : wkv;
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += dn[e] * wv[e] * xv[e] * r;
+      dot = group_sum(dot, LP) / (float)DH;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xh = xv[e] * r;
+        o[e] = r * (dn[e] * wv[e] - xh * dot);
+        if (valid) {
+          if (isq) aq[e] += dn[e] * xh;
+          else ak[e] += dn[e] * xh;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = dn[e];
+    }
+    if (valid) V8<T>::store(out + t * ld_out + (int64_t)hh * DH + 8 * j, o);
+  }
+  if (!qk_norm) return;
+  // Lanes with the same j hold partials of the same 8 weights.
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    for (int o2 = LP; o2 < 64; o2 <<= 1) {
+      aq[e] += __shfl_xor(aq[e], o2, 64);
+      ak[e] += __shfl_xor(ak[e], o2, 64);
+    }
+  }
+  const int wave = threadIdx.x >> 6;
+  for (int w = 0; w < 4; ++w) {   // fixed order across waves
+    if (wave == w && lane < LP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq[8 * j + e] += aq[e];
+        sk[8 * j + e] += ak[e];
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < DH; i += 256) {
+    wq_part[(int64_t)blockIdx.x * DH + i] = sq[i];
+    wk_part[(int64_t)blockIdx.x * DH + i] = sk[i];
+  }
+}
+
+constexpr int kQkBwdParts = 512;
+
+template <class T>
+hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
+                         const float* rstd, const void* w, const void* resid,
+                         int resid_f32, void* dx, float* dx32, float* wpart,
+                         int* nparts, hipStream_t s) {
+  const int cpl = (int)cdiv(n, 512);
+  int64_t grid = cdiv(rows, 4 * 8);  // at least 8 rows per wave
+  if (grid > kNormBwdParts) grid = kNormBwdParts;
+  if (grid < 1) grid = 1;
+  *nparts = (int)grid;
+  const size_t shm = (size_t)n * sizeof(float);
+#define Q3L_RB(C)                                                              \
+  hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, C>), dim3(grid), dim3(256), shm, s, \
+                     rows, n, (const T*)dy, (const T*)x, rstd, (const T*)w,    \
+                     resid, resid_f32, (T*)dx, dx32, wpart)
+  if (cpl <= 1) Q3L_RB(1);
+  else if (cpl <= 2) Q3L_RB(2);
+  else if (cpl <= 4) Q3L_RB(4);
+  else if (cpl <= 8) Q3L_RB(8);
+  else if (cpl <= 16) Q3L_RB(16);
+  else return hipErrorInvalidValue;
+#undef Q3L_RB
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int rmsnorm_bwd_max_parts() { return kNormBwdParts; }
+int qknorm_bwd_max_parts() { return kQkBwdParts; }
+
+hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
+                       const void* w, float eps, void* y, float* rstd,
+                       hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, grid, block, 0, s, rows, n,
+                       (const bf16_t*)x, (const bf16_t*)w, eps, (bf16_t*)y, rstd);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, block, 0, s, rows, n,
+                       (const float*)x, (const float*)w, eps, (float*)y, rstd);
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
+                       const void* x, const float* rstd, const void* w,
+                       const void* resid, int resid_f32, void* dx,
+                       float* dx32, float* wpart, int* nparts, hipStream_t s) {
+  if (dtype == 1)
+    return rmsnorm_bwd_t<bf16_t>(rows, n, dy, x, rstd, w, resid, resid_f32, dx,
+                                 dx32, wpart, nparts, s);
+  return rmsnorm_bwd_t<float>(rows, n, dy, x, rstd, w, resid, resid_f32, dx,
+                              dx32, wpart, nparts, s);
+}
+
+hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
+                       int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256),
+                     0, s, part, nparts, n, out, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t rope_table(int L, int d_h, float theta, float* cos_t, float* sin_t,
+                      hipStream_t s) {
+  const int n = L * (d_h / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256),
+                     0, s, L, d_h, (double)theta, cos_t, sin_t);
+  return hipGetLastError();
+}
+
+hipError_t qknorm_rope_fwd(int dtype, int B, int L, int h_q, int h_kv,
+                           int d_h, int qk_norm, float eps, const void* in,
+                           int64_t ld_in, const void* wq, const void* wk,
+                           const float* cos_t, const float* sin_t, void* out,
+                           int64_t ld_out, float* rstd_q, float* rstd_k,
+                           hipStream_t s) {
+  const int64_t tokens = (int64_t)B * L;
+  const int64_t threads = tokens * (h_q + h_kv) * (d_h / 8);
+  dim3 grid((unsigned)cdiv(threads, 256)), block(256);
+#define Q3L_QF(T, D)                                                          \
+  hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, D>), grid, block, 0, s,       \
+                     tokens, L, h_q, h_kv, qk_norm, eps, (const T*)in, ld_in, \
+                     (const T*)wq, (const T*)wk, cos_t, sin_t, (T*)out,       \
+                     ld_out, rstd_q, rstd_k)
+  if (dtype == 1) {
+    if (d_h == 128) Q3L_QF(bf16_t, 128); else Q3L_QF(bf16_t, 64);
+  } else {
+    if (d_h == 128) Q3L_QF(float, 128); else Q3L_QF(float, 64);
+  }
+#undef Q3L_QF
+  return hipGetLastError();
+}
+
+hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
+                           int d_h, int qk_norm, const void* g_in,
+                           int64_t ld_g, const void* pre, int64_t ld_pre,
+                           const void* wq, const void* wk, const float* rstd_q,
+                           const float* rstd_k, const float* cos_t,
+                           const float* sin_t, void* out, int64_t ld_out,
+                           float* wq_part, float* wk_part, int* nparts,
+                           hipStream_t s) {
+  const int64_t tokens = (int64_t)B * L;
+  const int64_t items = tokens * (h_q + h_kv);
+  const int per_block = 256 / (d_h / 8);
+  int64_t grid = cdiv(items, (int64_t)per_block * 8);
+  if (grid > kQkBwdParts) grid = kQkBwdParts;
+  if (grid < 1) grid = 1;
+  *nparts = (int)grid;
+#define Q3L_QB(T, D)                                                            \
+  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T, D>), dim3(grid), dim3(256), 0, s, \
+                     tokens, L, h_q, h_kv, qk_norm, (const T*)g_in, ld_g,       \
+                     (const T*)pre, ld_pre, (const T*)wq, (const T*)wk, rstd_q, \
+                     rstd_k, cos_t, sin_t, (T*)out, ld_out, wq_part, wk_part)
+  if (dtype == 1) {
+    if (d_h == 128) Q3L_QB(bf16_t, 128); else Q3L_QB(bf16_t, 64);
+  } else {
+    if (d_h == 128) Q3L_QB(float, 128); else Q3L_QB(float, 64);
+  }
+#undef Q3L_QB
+  return hipGetLastError();
+}
+
+}  // namespace q3l

@@ -1,0 +1,124 @@
+// Internal launch interface between the host orchestration (api.cpp) and the
+// kernels.  Every launcher enqueues on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3l {
+
+// A GEMM operand viewed as a [rows x K] matrix that is staged into LDS with K
+// contiguous.  Two storage forms:
+//  - k_contig = 1: element (r, k) at p[s][(r - start[s]) * ld[s] + k], the
+//    segment s chosen by r (weights stored [out, in], activations [T, f]).
+//    paired = 1 interleaves two segments in 32-row blocks: logical row r
+//    reads segment (r / 32) % 2, row (r / 64) * 32 + r % 32 (the gate/up pair).
+//  - k_contig = 0: element (r, k) at p[s][(k - start[s]) * ld[s] + r], the
+//    segment s chosen by k (a weight read as [in, out], or activations read
+//    transposed for a weight gradient).
+struct Operand {
+  const void* p[3];
+  int64_t ld[3];
+  int32_t start[3];
+  int32_t nseg;
+  int32_t rows;      // valid rows (for paired: rows of ONE segment)
+  int32_t k_contig;
+  int32_t paired;
+};
+
+enum EpiKind : int32_t {
+  EPI_STORE = 0,     // C = acc (+ R)                      dtype C, R
+  EPI_PARTIAL = 1,   // P = acc fp32; H = R + acc (opt.)    fp32 P, dtype H
+  EPI_SILU_MUL = 2,  // paired gate/up: G|U (opt.), F = silu(g) * u
+  EPI_SILU_BWD = 3,  // df tile + saved g, u -> dg, du
+  EPI_WGRAD = 4      // fp32 C (+)= acc, C split by M segments
+};
+
+struct Epilogue {
+  int32_t kind;
+  void* c;          // STORE: C; PARTIAL: H (may be null); SILU_MUL: F;
+                    // SILU_BWD: dG|dU base
+  int64_t ldc;
+  const void* r;    // STORE / PARTIAL: residual (may be null);
+                    // SILU_BWD: saved G|U base
+  int64_t ldr;
+  float* p32;       // PARTIAL: fp32 partial
+  int64_t ldp;
+  void* gu;         // SILU_MUL: saved G|U base (may be null)
+  int64_t ldgu;
+  int32_t ffn;      // SILU_*: d_ffn (U starts at column ffn of G|U)
+  // WGRAD
+  float* cs[3];
+  int32_t cstart[3];
+  int32_t cnseg;
+  int32_t accumulate;
+};
+
+struct GemmArgs {
+  Operand a, b;       // C[M, N] = sum_k A(m, k) B(n, k)
+  int32_t M, N, K;    // N is the logical width (paired: 2 * round_up(ffn, 32))
+  Epilogue epi;
+};
+
+// bf16 MFMA GEMM (K must be a multiple of 8; every k_contig = 0 operand's
+// rows a multiple of 8).
+hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
+// Plain fp32 GEMM with the same argument structure (correctness path).
+hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
+
+// ---- norms / RoPE / elementwise (dtype: 0 fp32, 1 bf16) -------------------
+hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
+                       const void* w, float eps, void* y, float* rstd,
+                       hipStream_t s);
+// dx = resid + rmsnorm_backward(dy);  dw partial sums per block into
+// wpart[nblocks_out][n] (fp32).  Returns the number of partial rows written
+// through *nparts.  resid may be fp32 (resid_f32=1) or dtype; dx_f32 (opt.)
+// receives dx in fp32 as well.
+hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
+                       const void* x, const float* rstd, const void* w,
+                       const void* resid, int resid_f32, void* dx,
+                       float* dx_f32, float* wpart, int* nparts,
+                       hipStream_t s);
+int rmsnorm_bwd_max_parts();
+// out[n] (+)= sum_p part[p][n]
+hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
+                       int accumulate, hipStream_t s);
+hipError_t rope_table(int L, int d_h, float theta, float* cos_t, float* sin_t,
+                      hipStream_t s);
+// q/k norm + RoPE over the q and k heads of a [T, ld_in] buffer.
+hipError_t qknorm_rope_fwd(int dtype, int B, int L, int h_q, int h_kv,
+                           int d_h, int qk_norm, float eps, const void* in,
+                           int64_t ld_in, const void* wq, const void* wk,
+                           const float* cos_t, const float* sin_t, void* out,
+                           int64_t ld_out, float* rstd_q, float* rstd_k,
+                           hipStream_t s);
+hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
+                           int d_h, int qk_norm, const void* g_in,
+                           int64_t ld_g, const void* pre, int64_t ld_pre,
+                           const void* wq, const void* wk, const float* rstd_q,
+                           const float* rstd_k, const float* cos_t,
+                           const float* sin_t, void* out, int64_t ld_out,
+                           float* wq_part, float* wk_part, int* nparts,
+                           hipStream_t s);
+int qknorm_bwd_max_parts();
+// Elementwise conversions used by the correctness path.
+hipError_t add_f32_to(int dtype, int64_t n, const float* a, void* out,
+                      hipStream_t s);
+
+// ---- attention ------------------------------------------------------------
+struct AttnArgs {
+  int B, L, h_q, h_kv, d_h;
+  const void* q; int64_t ldq;
+  const void* k; int64_t ldk;
+  const void* v; int64_t ldv;
+  void* o; int64_t ldo;
+  float* lse;
+  // backward only
+  const void* dout; int64_t lddo;
+  void* dq; void* dk; void* dv;   // strides ldq / ldk / ldv
+  float* delta;                   // [B, h_q, L] scratch
+};
+hipError_t attn_fwd(int dtype, const AttnArgs& a, hipStream_t s);
+hipError_t attn_bwd(int dtype, const AttnArgs& a, hipStream_t s);
+
+}  // namespace q3l
