@@ -105,8 +105,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   constexpr int KCH = KT * DH / 8 / 256;  // 16-byte K chunks per thread
   u32x4_t kreg[KCH];
   u32x4_t vreg[8];
+  // V^T blocks: key-block index fastest over lanes (conflict-free LDS stores).
   const bool vact = tid < (KT / 8) * (DH / 8);
-  const int vdb = tid % (DH / 8), vkb = tid / (DH / 8);
+  const int vkb = tid % (KT / 8), vdb = tid / (KT / 8);
   auto load_tile = [&](int t) {
     const int kv0 = t * KT;
 #pragma unroll
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
 
   // Loader: threads 0..127 own one 8x8 block of Q, 128..255 one of dO.
   const int sel = tid >> 7, bt = tid & 127;
-  const int db = bt % (DH / 8), qb = bt / (DH / 8);   // qb < QT/8 when DH=128
-  const bool lact = qb < QT / 8;
+  const int qb = bt % (QT / 8), db = bt / (QT / 8);
+  const bool lact = db < DH / 8;
   u32x4_t reg[8];
   float lreg = 0.f;
   auto load_tile = [&](int it) {
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   constexpr int KCH = KT * DH / 8 / 256;
   u32x4_t kreg[KCH], vreg[KCH], treg[8];
   const bool tact = tid < (KT / 8) * (DH / 8);
-  const int tdb = tid % (DH / 8), tkb = tid / (DH / 8);
+  const int tkb = tid % (KT / 8), tdb = tid / (KT / 8);
   auto load_tile = [&](int t) {
     const int kv0 = t * KT;
 #pragma unroll

@@ -5,16 +5,25 @@
 // C[M, N] = sum_k A(m, k) B(n, k), fp32 accumulation.
 //
 // Design (one workgroup = 4 wave64s = one BM x BN output tile):
-//  - K is consumed in slabs of 64.  Each slab of A and B is staged in LDS
-//    as [rows][64 + 8] bf16 (the 8-element pad makes the 16-byte fragment
-//    reads of 16 consecutive rows hit distinct banks).  Two LDS stages:
-//    the next slab's global loads are in flight while the matrix cores work
-//    on the current one; one barrier per slab.
-//  - Operands whose rows are not K-contiguous in memory (a weight read as
-//    [in, out] for an input gradient, activations read along the token axis
-//    for a weight gradient) are loaded as 8 rows of 16 bytes and transposed
-//    8x8 in registers before the LDS store, so every operand sits in LDS
-//    K-contiguous and the inner loop is identical for all layouts.
+//  - K is consumed in slabs of 64.  Both operands of a slab go from HBM
+//    straight into LDS with buffer loads (buffer_load_dwordx4 ... lds): no
+//    staging registers and no LDS store instructions.  Each wave-instruction
+//    fills 1 KiB of LDS, lane i the i-th 16 bytes; lanes pick the global
+//    chunk that belongs at their position.  Out-of-range k (the K tail) uses
+//    an offset past the buffer's range, which the hardware returns as zero.
+//    Two LDS stages: the next slab streams in while the matrix cores work on
+//    the current one; one barrier per slab.
+//  - An operand whose rows are K-contiguous in memory (activations [T, f],
+//    weights [out, in]) sits in LDS as [rows][64] with the 16-byte chunks of
+//    row r XOR-swizzled by (r >> 1) & 7, so the 16-byte fragment reads of 16
+//    consecutive rows hit 16 distinct bank groups.
+//  - An operand that is contiguous along its rows instead (a weight read as
+//    [in, out] for an input gradient; activations read along the token axis
+//    for a weight gradient) sits in LDS as it is in memory, [64][rows], with
+//    chunks of k-row kr swizzled by 4 * (kr & 3), and is read with the
+//    gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group
+//    lane j receives column j of four consecutive k-rows, exactly the K-major
+//    fragment the matrix instruction wants.  No register transposes.
 //  - The waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile of
 //    32x32 accumulators (v_mfma_f32_32x32x16_bf16).  The B fragment is
 //    passed as the MFMA's first operand so each lane ends up holding four
@@ -33,110 +42,166 @@ namespace q3l {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;
+constexpr uint32_t kOOB = 0x80000000u;   // any offset past the buffer range
 
-__device__ inline int seg_of(const int32_t* start, int nseg, int idx) {
-  int s = 0;
-  if (nseg > 1 && idx >= start[1]) s = 1;
-  if (nseg > 2 && idx >= start[2]) s = 2;
-  return s;
+#define Q3L_LDS __attribute__((address_space(3)))
+
+__device__ inline uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint64_t uni64(uint64_t v) {
+  return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v);
 }
 
-// ---- operand loaders ------------------------------------------------------
-// K-contiguous source: each thread moves 16-byte chunks of ROWS/32 rows; the
-// chunk column (kc) is fixed per thread, so row addresses are set up once.
-template <int ROWS>
-struct KLoader {
-  static constexpr int NCH = ROWS / 32;
-  const bf16_t* rp[NCH];
-  u32x4_t reg[NCH];
-  int kc, rl;
+// 16 bytes per lane from a raw buffer straight into LDS: lane i's data lands
+// at LDS byte lds_base + 16 * i.  The buffer covers [p, p + 2 GiB) with
+// stride 0, so `voff` is a byte offset and any offset >= 2^31 reads zeros.
+// Issued as inline asm: the compiler then does not treat the pending LDS
+// writes as aliasing every LDS read of the current slab (it would otherwise
+// wait for the next slab's loads before reading this one).  The kernel waits
+// for these loads itself (s_waitcnt vmcnt(0) before each slab's barrier).
+typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
+__device__ inline void dma16(uint64_t p, uint32_t voff, uint32_t lds_base) {
+  const u32x4s_t rsrc = {(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu,
+                         0x00020000u};
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr(const Q3L_LDS char* p) {
+  return (uint32_t)(uintptr_t)p;
+}
 
-  __device__ void init(const Operand& o, int r0, int tid) {
-    kc = tid & 7;
-    rl = tid >> 3;
+// Segment holding index idx of an operand (idx uniform): base pointer, ld
+// (elements) and start.  Every field is read from the kernel argument through
+// readfirstlane before the select, so the compiler keeps the choice between
+// register values instead of folding it into an indexed load of the table.
+__device__ inline void pick(const Operand& o, int idx, uint64_t& p, int64_t& ld, int& st) {
+  const int n = (int)uni((uint32_t)o.nseg);
+  const int s1 = n > 1 ? (int)uni((uint32_t)o.start[1]) : 0x7fffffff;
+  const int s2 = n > 2 ? (int)uni((uint32_t)o.start[2]) : 0x7fffffff;
+  const uint64_t p0 = uni64((uint64_t)o.p[0]);
+  const uint64_t p1 = uni64((uint64_t)o.p[n > 1 ? 1 : 0]);
+  const uint64_t p2 = uni64((uint64_t)o.p[n > 2 ? 2 : 0]);
+  const int64_t l0 = (int64_t)uni64((uint64_t)o.ld[0]);
+  const int64_t l1 = (int64_t)uni64((uint64_t)o.ld[n > 1 ? 1 : 0]);
+  const int64_t l2 = (int64_t)uni64((uint64_t)o.ld[n > 2 ? 2 : 0]);
+  const bool b1 = idx >= s1, b2 = idx >= s2;
+  p = b2 ? p2 : (b1 ? p1 : p0);
+  ld = b2 ? l2 : (b1 ? l1 : l0);
+  st = b2 ? s2 : (b1 ? s1 : 0);
+}
+
+// ---- K-contiguous operand: [R rows][64 k] in LDS ---------------------------
+// Wave-instruction q (= 4 * i + wave) fills LDS rows 8q .. 8q+7; lane l writes
+// row 8q + l/8, slot l%8, holding global chunk (slot ^ swz(row)) of that row.
+template <int R>
+struct KOperand {
+  static constexpr int NI = R / 32;   // wave-instructions per thread per slab
+  uint32_t voff[NI];   // per lane: byte offset of its chunk at k = 0
+  int kel[NI];         // per lane: first k (elements) of its chunk at k0 = 0
+  uint64_t base[NI];   // uniform: segment base of the instruction's rows
+
+  __device__ void init(const Operand& o, int r0, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      int r = r0 + rl + 32 * i;
-      int seg, rr;
+    for (int i = 0; i < NI; ++i) {
+      const int q = 4 * i + wave;
+      const int row = 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      kel[i] = 8 * c;
+      int gr = r0 + row;
+      uint64_t p;
+      int64_t ld;
+      int st;
       if (o.paired) {
-        seg = (r >> 5) & 1;
-        rr = (r >> 6) * 32 + (r & 31);
-        if (rr >= o.rows) rr = o.rows - 1;
-        rp[i] = static_cast<const bf16_t*>(o.p[seg]) + (int64_t)rr * o.ld[seg];
+        const int g0 = r0 + 8 * q;        // uniform: first logical row
+        const bool up = (g0 >> 5) & 1;
+        const uint64_t pg = uni64((uint64_t)o.p[0]), pu = uni64((uint64_t)o.p[1]);
+        const int64_t lg = (int64_t)uni64((uint64_t)o.ld[0]);
+        const int64_t lu = (int64_t)uni64((uint64_t)o.ld[1]);
+        p = up ? pu : pg;
+        ld = up ? lu : lg;
+        int pr = (gr >> 6) * 32 + (gr & 31);
+        if (pr >= o.rows) pr = o.rows - 1;
+        voff[i] = (uint32_t)((int64_t)pr * ld * 2 + 16 * c);
       } else {
-        rr = r < o.rows ? r : o.rows - 1;
-        seg = seg_of(o.start, o.nseg, rr);
-        rp[i] = static_cast<const bf16_t*>(o.p[seg]) +
-                (int64_t)(rr - o.start[seg]) * o.ld[seg];
+        int g0 = r0 + 8 * q;
+        if (g0 > o.rows - 1) g0 = o.rows - 1;
+        pick(o, g0, p, ld, st);
+        if (gr > o.rows - 1) gr = o.rows - 1;
+        voff[i] = (uint32_t)((int64_t)(gr - st) * ld * 2 + 16 * c);
       }
+      base[i] = p;
     }
   }
-  __device__ void load(int k0, int K) {
-    const int k = k0 + kc * 8;
+  // Issue the slab starting at k0 into LDS stage `dst` (R * 128 bytes).
+  __device__ void issue(const Operand&, int k0, int K, Q3L_LDS char* dst,
+                        int wave) const {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      reg[i] = (k < K) ? ld16(rp[i] + k) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  __device__ void store(bf16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) st16(lds + (rl + 32 * i) * LDK + kc * 8, reg[i]);
-  }
-};
-
-// Row-contiguous source (element (r, k) at p[(k - start) * ld + r]): each
-// active thread owns one 8 (rows) x 8 (k) block, loads it as 8 k-rows of 16
-// bytes (consecutive threads read consecutive 16-byte column chunks) and
-// transposes it in registers.
-template <int ROWS>
-struct TLoader {
-  u32x4_t reg[8];
-  int rb, kb, col;
-  bool active;
-
-  __device__ void init(const Operand& o, int r0, int tid) {
-    active = tid < ROWS;
-    rb = tid % (ROWS / 8);
-    kb = tid / (ROWS / 8);
-    col = r0 + 8 * rb;
-    if (col > o.rows - 8) col = o.rows - 8;
-  }
-  __device__ void load(const Operand& o, int k0, int K) {
-    if (!active) return;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int k = k0 + 8 * kb + r;
-      if (k < K) {
-        const int s = seg_of(o.start, o.nseg, k);
-        reg[r] = ld16(static_cast<const bf16_t*>(o.p[s]) +
-                      (int64_t)(k - o.start[s]) * o.ld[s] + col);
-      } else {
-        reg[r] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t off = (k0 + kel[i] < K) ? voff[i] + 2u * (uint32_t)k0 : kOOB;
+      dma16(base[i], off, uni(lds_addr(dst + 1024 * (4 * i + wave))));
     }
   }
-  __device__ void store(bf16_t* lds) const {
-    if (!active) return;
-    u32x4_t t[8];
-    transpose8x8(reg, t);
+};
+
+// ---- row-contiguous operand: [64 k][R] in LDS, read transposed -------------
+// CPR 16-byte chunks per k-row; wave-instruction q fills k-rows RPI*q ..;
+// lane l writes k-row RPI*q + l/CPR, slot l%CPR, holding global chunk
+// slot ^ (4 * (krow & 3)).
+template <int R>
+struct ROperand {
+  static constexpr int NI = R / 32;
+  static constexpr int CPR = R / 8;
+  static constexpr int RPI = 64 / CPR;
+  int col[NI];     // per lane: global column of its chunk (clamped)
+  int krl[NI];     // per lane: k-row within the slab
+
+  __device__ void init(const Operand& o, int r0, int wave, int lane) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st16(lds + (8 * rb + c) * LDK + 8 * kb, t[c]);
+    for (int i = 0; i < NI; ++i) {
+      const int q = 4 * i + wave;
+      const int kr = RPI * q + lane / CPR;
+      const int c = (lane % CPR) ^ (4 * (kr & 3));
+      int n = r0 + 8 * c;
+      if (n > o.rows - 8) n = o.rows - 8;
+      col[i] = n;
+      krl[i] = kr;
+    }
+  }
+  __device__ void issue(const Operand& o, int k0, int K, Q3L_LDS char* dst,
+                        int wave) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = 4 * i + wave;
+      int kq = k0 + RPI * q;                    // uniform first k-row
+      if (kq > K - 1) kq = K - 1;
+      uint64_t p;
+      int64_t ld;
+      int st;
+      pick(o, kq, p, ld, st);
+      const int k = k0 + krl[i];
+      const uint32_t off =
+          k < K ? (uint32_t)(((int64_t)(k - st) * ld + col[i]) * 2) : kOOB;
+      dma16(p, off, uni(lds_addr(dst + 1024 * (4 * i + wave))));
+    }
   }
 };
 
-template <int ROWS, bool KC> struct LoaderSel;
-template <int ROWS> struct LoaderSel<ROWS, true> {
-  KLoader<ROWS> l;
-  __device__ void init(const Operand& o, int r0, int tid) { l.init(o, r0, tid); }
-  __device__ void load(const Operand&, int k0, int K) { l.load(k0, K); }
-  __device__ void store(bf16_t* lds) const { l.store(lds); }
-};
-template <int ROWS> struct LoaderSel<ROWS, false> {
-  TLoader<ROWS> l;
-  __device__ void init(const Operand& o, int r0, int tid) { l.init(o, r0, tid); }
-  __device__ void load(const Operand& o, int k0, int K) { l.load(o, k0, K); }
-  __device__ void store(bf16_t* lds) const { l.store(lds); }
-};
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x4_t ld_lds16(const Q3L_LDS char* p) {
+  return *reinterpret_cast<const Q3L_LDS u32x4_t*>(p);
+}
+__device__ inline u32x4_t ld_tr2(const Q3L_LDS char* p, int second) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (Q3L_LDS i16x4_t*)(p));
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (Q3L_LDS i16x4_t*)(p + second));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
 
 // ---- tile order -----------------------------------------------------------
 __device__ inline void map_tile(int bid, int nb, int ntm, int ntn, int& tm,
@@ -157,26 +222,84 @@ __device__ inline void map_tile(int bid, int nb, int ntm, int ntn, int& tm,
   tn = local / gsz;
 }
 
-__device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g); v_rcp_f32 (1 ulp) instead of an IEEE division.
+__device__ inline float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ inline float silu_f(float g) { return g * sigmoid_f(g); }
+
+// ---- fragment readers -----------------------------------------------------
+// K-contiguous tile [rows][64]: lane reads row wb + 32*i + lane%32, k-chunk
+// 2*kk + lane/32 (swizzled).  Addresses: lane base + per-kk offset + 4 KiB*i.
+template <int TT>
+struct KFrag {
+  uint32_t base;
+  uint32_t koff[4];
+  __device__ void init(int wb, int lane) {
+    const int r = wb + (lane & 31), h = lane >> 5, sw = ((lane & 31) >> 1) & 7;
+    base = (uint32_t)r * 128u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
+  }
+  __device__ void read(const Q3L_LDS char* t, int kk, u32x4_t f[TT]) const {
+#pragma unroll
+    for (int i = 0; i < TT; ++i) f[i] = ld_lds16(t + base + koff[kk] + 4096 * i);
+  }
+};
+// Row-contiguous tile [64][R] (row stride 2R bytes), transposed reads: in
+// 16-lane group g, lane s points at k-row 8*(g/2) + s/4 (+4 for the second
+// read), columns wb + 32*i + 16*(g%2) + 4*(s%4) .. +3 (chunks swizzled by
+// 4 * (k-row & 3)).
+template <int TT, int R>
+struct RFrag {
+  uint32_t base[TT];
+  __device__ void init(int wb, int lane) {
+    const int g = (lane >> 4) & 3, sl = lane & 15;
+    const uint32_t rowoff = (uint32_t)(8 * (g >> 1) + (sl >> 2)) * (2 * R) + 8 * (sl & 1);
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      const int chunk = (((wb + 32 * i) >> 3) ^ (4 * (sl >> 2))) | (2 * (g & 1) + ((sl & 3) >> 1));
+      base[i] = rowoff + (uint32_t)chunk * 16u;
+    }
+  }
+  __device__ void read(const Q3L_LDS char* t, int kk, u32x4_t f[TT]) const {
+#pragma unroll
+    for (int i = 0; i < TT; ++i) f[i] = ld_tr2(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
+  }
+};
+
+template <int ROWS, int TT, bool KC> struct OpSel;
+template <int ROWS, int TT> struct OpSel<ROWS, TT, true> {
+  KOperand<ROWS> ld;
+  KFrag<TT> fr;
+};
+template <int ROWS, int TT> struct OpSel<ROWS, TT, false> {
+  ROperand<ROWS> ld;
+  RFrag<TT, ROWS> fr;
+};
 
 // ---- the kernel -----------------------------------------------------------
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][(BM + BN) * LDK];
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
   const int wm = wave >> 1, wn = wave & 1;
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   int tm, tn;
   map_tile(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  LoaderSel<BM, AK> la;
-  LoaderSel<BN, BKC> lb;
-  la.init(g.a, m0, tid);
-  lb.init(g.b, n0, tid);
+  OpSel<BM, TM, AK> oa;
+  OpSel<BN, TN, BKC> ob;
+  oa.ld.init(g.a, m0, wave, lane);
+  ob.ld.init(g.b, n0, wave, lane);
+  oa.fr.init(wm * WM, lane);
+  ob.fr.init(wn * WN, lane);
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -187,41 +310,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (g.K + BK - 1) / BK;
-  la.load(g.a, 0, g.K);
-  lb.load(g.b, 0, g.K);
-  la.store(lds[0]);
-  lb.store(lds[0] + BM * LDK);
-  __syncthreads();
-
-  const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
-  const int kof = (lane >> 5) * 8;
+  oa.ld.issue(g.a, 0, g.K, lds, wave);
+  ob.ld.issue(g.b, 0, g.K, lds + ABYTES, wave);
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(g.a, (kt + 1) * BK, g.K);
-      lb.load(g.b, (kt + 1) * BK, g.K);
+    // This wave's loads of slab kt are done; the barrier makes every wave's
+    // visible and guarantees slab kt-1 (in the other stage) is fully read.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) {
+      Q3L_LDS char* nx = lds + ((kt + 1) & 1) * STAGE;
+      oa.ld.issue(g.a, (kt + 1) * BK, g.K, nx, wave);
+      ob.ld.issue(g.b, (kt + 1) * BK, g.K, nx + ABYTES, wave);
     }
-    const bf16_t* As = lds[kt & 1];
-    const bf16_t* Bs = As + BM * LDK;
+    const Q3L_LDS char* As = lds + (kt & 1) * STAGE;
+    const Q3L_LDS char* Bs = As + ABYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       u32x4_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = ld16(As + (arow + i * 32) * LDK + kk * 16 + kof);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = ld16(Bs + (brow + j * 32) * LDK + kk * 16 + kof);
+      oa.fr.read(As, kk, af);
+      ob.fr.read(Bs, kk, bfr);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
     }
-    if (more) {
-      la.store(lds[(kt + 1) & 1]);
-      lb.store(lds[(kt + 1) & 1] + BM * LDK);
-    }
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds C[m][n..n+3] for each (i, j, q) ----
@@ -292,7 +404,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
             float dg[4], du[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float sg = 1.0f / (1.0f + __expf(-gg[r]));
+              const float sg = sigmoid_f(gg[r]);
               dg[r] = v[r] * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
               du[r] = v[r] * gg[r] * sg;
             }
@@ -300,9 +412,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
             st8(D, u32x2_t{pack2(dg[0], dg[1]), pack2(dg[2], dg[3])});
             st8(D + e.ffn, u32x2_t{pack2(du[0], du[1]), pack2(du[2], du[3])});
           } else if constexpr (EPI == EPI_WGRAD) {
-            const int s = seg_of(e.cstart, e.cnseg, m);
-            f32x4_t* C = reinterpret_cast<f32x4_t*>(
-                e.cs[s] + (int64_t)(m - e.cstart[s]) * e.ldc + n);
+            const bool s1 = e.cnseg > 1 && m >= e.cstart[1];
+            const bool s2 = e.cnseg > 2 && m >= e.cstart[2];
+            float* cb = s2 ? e.cs[2] : (s1 ? e.cs[1] : e.cs[0]);
+            const int cst = s2 ? e.cstart[2] : (s1 ? e.cstart[1] : e.cstart[0]);
+            f32x4_t* C = reinterpret_cast<f32x4_t*>(cb + (int64_t)(m - cst) * e.ldc + n);
             f32x4_t nv{v[0], v[1], v[2], v[3]};
             if (e.accumulate) nv += *C;
             *C = nv;

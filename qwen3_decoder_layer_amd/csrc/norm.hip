@@ -160,14 +160,26 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
 constexpr int kNormBwdParts = 256;
 
 // ---- column reduction of partial rows -------------------------------------
+// A workgroup owns 64 columns; its 4 waves sum interleaved quarters of the
+// partial rows (lanes over columns: 256-byte coalesced reads), then combine
+// in a fixed order.
 __global__ __launch_bounds__(256) void reduce_rows_kernel(
     const float* __restrict__ part, int nparts, int n, float* __restrict__ out,
     int accumulate) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * n + i];
-  out[i] = accumulate ? out[i] + s : s;
+  if (i < n) {
+#pragma unroll 8
+    for (int p = wave; p < nparts; p += 4) s += part[(int64_t)p * n + i];
+  }
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && i < n) {
+    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    out[i] = accumulate ? out[i] + t : t;
+  }
 }
 
 // ---- RoPE angle table: angle(t, i) = t * theta^(-2i/d_h), in double --------
@@ -400,7 +412,7 @@ hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
 
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
                        int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256),
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 64)), dim3(256),
                      0, s, part, nparts, n, out, accumulate);
   return hipGetLastError();
 }
