@@ -89,6 +89,13 @@ q3l_status validate(const q3l_layer_cfg* c) {
     return fail(Q3L_EUNSUPPORTED, "sizes exceed the 32-bit index range");
   if (c->L > 65535LL * 32)
     return fail(Q3L_EUNSUPPORTED, "L=%d too long", c->L);
+  // The bf16 GEMM addresses each operand with 32-bit byte offsets.
+  if (c->dtype == Q3L_BF16) {
+    const int64_t widest_act = std::max<int64_t>(widest, (int64_t)c->d);
+    if ((T + 8) * widest_act * 2 >= (1LL << 31))
+      return fail(Q3L_EUNSUPPORTED, "B*L=%lld tokens x %lld features exceeds 2 GiB per "
+                  "activation tensor", (long long)T, (long long)widest_act);
+  }
   return Q3L_OK;
 }
 
@@ -117,8 +124,14 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
 }
 
 struct BwdWs {
-  size_t dgu, dhn, dh32, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart, total;
+  size_t dgu, dhn, dh32, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
+  // bf16 only: transposed weights ([in, out]) and two scratch buffers for the
+  // transposed operands of the weight-gradient GEMMs ([features, Tp]).
+  size_t wt_down, wt_gu, wt_o, wt_qkv, tA, tB;
+  size_t total;
 };
+
+int64_t pad8(int64_t v) { return (v + 7) / 8 * 8; }
 
 BwdWs bwd_layout(const q3l_layer_cfg& c) {
   const Dims m = dims_of(c);
@@ -137,6 +150,15 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
   w.wpart = take((size_t)rmsnorm_bwd_max_parts() * m.d * 4);
   w.qpart = take((size_t)qknorm_bwd_max_parts() * m.dh * 4);
   w.kpart = take((size_t)qknorm_bwd_max_parts() * m.dh * 4);
+  if (c.dtype == Q3L_BF16) {
+    const size_t Tp = (size_t)pad8(m.T);
+    w.wt_down = take((size_t)m.ffn * m.d * 2);
+    w.wt_gu = take((size_t)m.d * 2 * m.ffn * 2);
+    w.wt_o = take((size_t)m.qd * m.d * 2);
+    w.wt_qkv = take((size_t)m.d * m.nqkv * 2);
+    w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
+    w.tB = take((size_t)std::max<int64_t>(std::max<int64_t>(m.ffn, m.qd), m.d) * Tp * 2);
+  }
   w.total = off;
   return w;
 }
@@ -432,43 +454,84 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   float* kpart = reinterpret_cast<float*>(at(workspace, W.kpart));
   const int T = (int)m.T;
 
+  // bf16: every backward GEMM runs in the matrix-core kernel's K-contiguous
+  // form.  Weights are transposed to [in, out] once per call; the two
+  // operands of each weight-gradient GEMM are transposed to [features, T]
+  // (T padded to a multiple of 8 with zeros) into two reused scratch buffers.
+  const bool bt = dt == Q3L_BF16;
+  const int Tp = (int)pad8(m.T);
+  char* wt_down = bt ? at(workspace, W.wt_down) : nullptr;
+  char* wt_gu = bt ? at(workspace, W.wt_gu) : nullptr;
+  char* wt_o = bt ? at(workspace, W.wt_o) : nullptr;
+  char* wt_qkv = bt ? at(workspace, W.wt_qkv) : nullptr;
+  char* tA = bt ? at(workspace, W.tA) : nullptr;
+  char* tB = bt ? at(workspace, W.tB) : nullptr;
+  if (bt) {
+    Q3L_HIP(transpose_bf16(m.d, m.d, m.ffn, w->down, m.ffn, wt_down, m.d, s));
+    Q3L_HIP(transpose_bf16(m.ffn, m.ffn, m.d, w->gate, m.d, wt_gu, 2 * m.ffn, s));
+    Q3L_HIP(transpose_bf16(m.ffn, m.ffn, m.d, w->up, m.d, wt_gu + (size_t)m.ffn * 2,
+                           2 * m.ffn, s));
+    Q3L_HIP(transpose_bf16(m.d, m.d, m.qd, w->o, m.qd, wt_o, m.d, s));
+    Q3L_HIP(transpose_bf16(m.qd, m.qd, m.d, w->q, m.d, wt_qkv, m.nqkv, s));
+    Q3L_HIP(transpose_bf16(m.kvd, m.kvd, m.d, w->k, m.d, wt_qkv + (size_t)m.qd * 2,
+                           m.nqkv, s));
+    Q3L_HIP(transpose_bf16(m.kvd, m.kvd, m.d, w->v, m.d,
+                           wt_qkv + (size_t)(m.qd + m.kvd) * 2, m.nqkv, s));
+  }
+  // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
+  // feature counts; A/B activations with row strides lda/ldb).
+  auto wgrad = [&](const void* A, int lda, int ma, const void* B, int ldb, int nb,
+                   Epilogue e) -> hipError_t {
+    GemmArgs g{};
+    if (bt) {
+      hipError_t err = transpose_bf16(T, Tp, ma, A, lda, tA, Tp, s);
+      if (err != hipSuccess) return err;
+      err = transpose_bf16(T, Tp, nb, B, ldb, tB, Tp, s);
+      if (err != hipSuccess) return err;
+      g.a = kop(tA, Tp, ma);
+      g.b = kop(tB, Tp, nb);
+      g.K = Tp;
+    } else {
+      g.a = rop(A, lda, ma);
+      g.b = rop(B, ldb, nb);
+      g.K = T;
+    }
+    g.M = ma; g.N = nb;
+    g.epi = e;
+    return gemm(dt, g, s);
+  };
+
   // Step 9 (down_proj): df = dy W_down, fused with the SwiGLU adjoint.
   {
     GemmArgs g{};
     g.a = kop(dy, m.d, T);
-    g.b = rop(w->down, m.ffn, m.ffn);
+    g.b = bt ? kop(wt_down, m.d, m.ffn) : rop(w->down, m.ffn, m.ffn);
     g.M = T; g.N = m.ffn; g.K = m.d;
     g.epi.kind = EPI_SILU_BWD;
     g.epi.c = dgu; g.epi.ldc = 2 * (int64_t)m.ffn;
     g.epi.r = gu; g.epi.ldr = 2 * (int64_t)m.ffn; g.epi.ffn = m.ffn;
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (want_w) {  // dW_down = dy^T f
-    GemmArgs g{};
-    g.a = rop(dy, m.d, m.d);
-    g.b = rop(f, m.ffn, m.ffn);
-    g.M = m.d; g.N = m.ffn; g.K = T;
-    g.epi = epi_wgrad(grads->down, m.ffn, acc);
-    Q3L_HIP(gemm(dt, g, s));
-  }
+  if (want_w)  // dW_down = dy^T f
+    Q3L_HIP(wgrad(dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc)));
   // Step 9 (gate/up): dhn = dg W_gate + du W_up (one GEMM over stacked K).
   {
     GemmArgs g{};
     g.a = kop(dgu, 2 * (int64_t)m.ffn, T);
-    g.b = rop(w->gate, m.d, m.d);
-    add_seg(g.b, w->up, m.d, m.ffn);
+    if (bt) {
+      g.b = kop(wt_gu, 2 * (int64_t)m.ffn, m.d);
+    } else {
+      g.b = rop(w->gate, m.d, m.d);
+      add_seg(g.b, w->up, m.d, m.ffn);
+    }
     g.M = T; g.N = m.d; g.K = 2 * m.ffn;
     g.epi = epi_store(dhn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
   if (want_w) {  // dW_gate | dW_up = [dg du]^T hn
-    GemmArgs g{};
-    g.a = rop(dgu, 2 * (int64_t)m.ffn, 2 * m.ffn);
-    g.b = rop(hn, m.d, m.d);
-    g.M = 2 * m.ffn; g.N = m.d; g.K = T;
-    g.epi = epi_wgrad(grads->gate, m.d, acc);
-    g.epi.cs[1] = grads->up; g.epi.cstart[1] = m.ffn; g.epi.cnseg = 2;
-    Q3L_HIP(gemm(dt, g, s));
+    Epilogue e = epi_wgrad(grads->gate, m.d, acc);
+    e.cs[1] = grads->up; e.cstart[1] = m.ffn; e.cnseg = 2;
+    Q3L_HIP(wgrad(dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e));
   }
   // Steps 8 and 10: post-attention RMSNorm adjoint plus the residual dy.
   {
@@ -481,19 +544,13 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   {
     GemmArgs g{};
     g.a = kop(dh, m.d, T);
-    g.b = rop(w->o, m.qd, m.qd);
+    g.b = bt ? kop(wt_o, m.d, m.qd) : rop(w->o, m.qd, m.qd);
     g.M = T; g.N = m.qd; g.K = m.d;
     g.epi = epi_store(dO, m.qd, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (want_w) {  // dW_o = dh^T O
-    GemmArgs g{};
-    g.a = rop(dh, m.d, m.d);
-    g.b = rop(ao, m.qd, m.qd);
-    g.M = m.d; g.N = m.qd; g.K = T;
-    g.epi = epi_wgrad(grads->o, m.qd, acc);
-    Q3L_HIP(gemm(dt, g, s));
-  }
+  if (want_w)  // dW_o = dh^T O
+    Q3L_HIP(wgrad(dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc)));
   // Step 5: attention backward (P recomputed from the log-sum-exp).
   {
     AttnArgs a{};
@@ -523,23 +580,23 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   {
     GemmArgs g{};
     g.a = kop(dqkv, m.nqkv, T);
-    g.b = rop(w->q, m.d, m.d);
-    add_seg(g.b, w->k, m.d, m.qd);
-    add_seg(g.b, w->v, m.d, m.qd + m.kvd);
+    if (bt) {
+      g.b = kop(wt_qkv, m.nqkv, m.d);
+    } else {
+      g.b = rop(w->q, m.d, m.d);
+      add_seg(g.b, w->k, m.d, m.qd);
+      add_seg(g.b, w->v, m.d, m.qd + m.kvd);
+    }
     g.M = T; g.N = m.d; g.K = m.nqkv;
     g.epi = epi_store(dxn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
   if (want_w) {  // dW_q | dW_k | dW_v = [dq dk dv]^T xn
-    GemmArgs g{};
-    g.a = rop(dqkv, m.nqkv, m.nqkv);
-    g.b = rop(xn, m.d, m.d);
-    g.M = m.nqkv; g.N = m.d; g.K = T;
-    g.epi = epi_wgrad(grads->q, m.d, acc);
-    g.epi.cs[1] = grads->k; g.epi.cstart[1] = m.qd;
-    g.epi.cs[2] = grads->v; g.epi.cstart[2] = m.qd + m.kvd;
-    g.epi.cnseg = 3;
-    Q3L_HIP(gemm(dt, g, s));
+    Epilogue e = epi_wgrad(grads->q, m.d, acc);
+    e.cs[1] = grads->k; e.cstart[1] = m.qd;
+    e.cs[2] = grads->v; e.cstart[2] = m.qd + m.kvd;
+    e.cnseg = 3;
+    Q3L_HIP(wgrad(dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e));
   }
   // Step 1: input RMSNorm adjoint plus the attention residual (fp32 dh).
   {

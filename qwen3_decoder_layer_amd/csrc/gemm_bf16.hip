@@ -5,25 +5,26 @@
 // C[M, N] = sum_k A(m, k) B(n, k), fp32 accumulation.
 //
 // Design (one workgroup = 4 wave64s = one BM x BN output tile):
-//  - K is consumed in slabs of 64.  Both operands of a slab go from HBM
-//    straight into LDS with buffer loads (buffer_load_dwordx4 ... lds): no
-//    staging registers and no LDS store instructions.  Each wave-instruction
-//    fills 1 KiB of LDS, lane i the i-th 16 bytes; lanes pick the global
-//    chunk that belongs at their position.  Out-of-range k (the K tail) uses
-//    an offset past the buffer's range, which the hardware returns as zero.
-//    Two LDS stages: the next slab streams in while the matrix cores work on
-//    the current one; one barrier per slab.
-//  - An operand whose rows are K-contiguous in memory (activations [T, f],
-//    weights [out, in]) sits in LDS as [rows][64] with the 16-byte chunks of
-//    row r XOR-swizzled by (r >> 1) & 7, so the 16-byte fragment reads of 16
-//    consecutive rows hit 16 distinct bank groups.
-//  - An operand that is contiguous along its rows instead (a weight read as
-//    [in, out] for an input gradient; activations read along the token axis
-//    for a weight gradient) sits in LDS as it is in memory, [64][rows], with
-//    chunks of k-row kr swizzled by 4 * (kr & 3), and is read with the
-//    gfx950 transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group
-//    lane j receives column j of four consecutive k-rows, exactly the K-major
-//    fragment the matrix instruction wants.  No register transposes.
+//  - K is consumed in slabs of KB (64).  A K-contiguous operand (activations
+//    [T, f], weights [out, in]) goes from HBM straight into LDS with buffer
+//    loads (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
+//    instructions.  Each wave-instruction fills 1 KiB of LDS, lane i the
+//    i-th 16 bytes; lanes pick the global chunk that belongs at their
+//    position.  Out-of-range k (the K tail) uses an offset past the buffer's
+//    range, which the hardware returns as zero.
+//  - An operand contiguous along its rows instead (a weight read as
+//    [in, out], activations read along the token axis) is also loaded
+//    straight into LDS, as it is in memory, and read with the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16).  That read sustains about a
+//    third of ds_read_b128's byte rate, so the layer's backward transposes
+//    its GEMM operands once (transpose.hip) and uses the K-contiguous path;
+//    the transposed-read path serves the stand-alone gradient entry points.
+//  - K-contiguous LDS tiles are [rows][KB] with the 16-byte chunks of row r XOR-swizzled
+//    by (r >> 1) & 7, so the 16-byte fragment reads of 16 consecutive rows
+//    hit 16 distinct bank groups.  Two LDS stages: the next slab streams in
+//    while the matrix cores work on the current one; one barrier per slab.
+//    Within a slab the next k-step's fragment reads are interleaved with
+//    the current step's matrix instructions (scheduling-group barriers).
 //  - The waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile of
 //    32x32 accumulators (v_mfma_f32_32x32x16_bf16).  The B fragment is
 //    passed as the MFMA's first operand so each lane ends up holding four
@@ -41,7 +42,6 @@
 namespace q3l {
 namespace {
 
-constexpr int BK = 64;
 constexpr uint32_t kOOB = 0x80000000u;   // any offset past the buffer range
 
 #define Q3L_LDS __attribute__((address_space(3)))
@@ -93,12 +93,22 @@ __device__ inline void pick(const Operand& o, int idx, uint64_t& p, int64_t& ld,
   st = b2 ? s2 : (b1 ? s1 : 0);
 }
 
-// ---- K-contiguous operand: [R rows][64 k] in LDS ---------------------------
-// Wave-instruction q (= 4 * i + wave) fills LDS rows 8q .. 8q+7; lane l writes
-// row 8q + l/8, slot l%8, holding global chunk (slot ^ swz(row)) of that row.
-template <int R>
+// ---- K-contiguous operand: [R rows][KB k] in LDS --------------------------
+// A row is KB*2 bytes = CPRK 16-byte chunks.  Wave-instruction q (= 4*i +
+// wave) fills rows RPW*q .. RPW*q + RPW-1; lane l writes row RPW*q + l/CPRK,
+// slot l%CPRK, holding global chunk (slot ^ swz(row)) of that row.  The
+// swizzle makes the fragment reads of 16 consecutive rows (same chunk)
+// conflict-free: KB=64: (row >> 1) & 7; KB=32: (row >> 2) & 3.
+template <int KB>
+__device__ inline int kswz(int row) {
+  return KB == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+template <int R, int KB>
 struct KOperand {
-  static constexpr int NI = R / 32;   // wave-instructions per thread per slab
+  static constexpr int CPRK = KB / 8;
+  static constexpr int RPW = 64 / CPRK;
+  static constexpr int NI = R / (4 * RPW);   // wave-instructions per thread per slab
   uint32_t voff[NI];   // per lane: byte offset of its chunk at k = 0
   int kel[NI];         // per lane: first k (elements) of its chunk at k0 = 0
   uint64_t base[NI];   // uniform: segment base of the instruction's rows
@@ -107,15 +117,15 @@ struct KOperand {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = 4 * i + wave;
-      const int row = 8 * q + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const int row = RPW * q + lane / CPRK;
+      const int c = (lane % CPRK) ^ kswz<KB>(row);
       kel[i] = 8 * c;
       int gr = r0 + row;
       uint64_t p;
       int64_t ld;
       int st;
       if (o.paired) {
-        const int g0 = r0 + 8 * q;        // uniform: first logical row
+        const int g0 = r0 + RPW * q;        // uniform: first logical row
         const bool up = (g0 >> 5) & 1;
         const uint64_t pg = uni64((uint64_t)o.p[0]), pu = uni64((uint64_t)o.p[1]);
         const int64_t lg = (int64_t)uni64((uint64_t)o.ld[0]);
@@ -126,7 +136,7 @@ struct KOperand {
         if (pr >= o.rows) pr = o.rows - 1;
         voff[i] = (uint32_t)((int64_t)pr * ld * 2 + 16 * c);
       } else {
-        int g0 = r0 + 8 * q;
+        int g0 = r0 + RPW * q;
         if (g0 > o.rows - 1) g0 = o.rows - 1;
         pick(o, g0, p, ld, st);
         if (gr > o.rows - 1) gr = o.rows - 1;
@@ -135,7 +145,7 @@ struct KOperand {
       base[i] = p;
     }
   }
-  // Issue the slab starting at k0 into LDS stage `dst` (R * 128 bytes).
+  // Issue the slab starting at k0 into LDS stage `dst` (R * KB * 2 bytes).
   __device__ void issue(const Operand&, int k0, int K, Q3L_LDS char* dst,
                         int wave) const {
 #pragma unroll
@@ -146,15 +156,20 @@ struct KOperand {
   }
 };
 
-// ---- row-contiguous operand: [64 k][R] in LDS, read transposed -------------
-// CPR 16-byte chunks per k-row; wave-instruction q fills k-rows RPI*q ..;
-// lane l writes k-row RPI*q + l/CPR, slot l%CPR, holding global chunk
-// slot ^ (4 * (krow & 3)).
-template <int R>
+// ---- row-contiguous operand: [KB k][R] in LDS, read transposed -------------
+// Element (r, k) at p[(k - start) * ld + r] (a weight read as [in, out], or
+// activations read along the token axis).  The tile sits in LDS as in
+// memory, [KB][R]: CPR 16-byte chunks per k-row; wave-instruction q fills
+// k-rows RPI*q ..; lane l writes k-row RPI*q + l/CPR, slot l%CPR, holding
+// global chunk slot ^ (4 * (krow & 3)).  Fragments are read with the gfx950
+// transposing LDS read.  (It runs at roughly a third of ds_read_b128's byte
+// rate, so the layer's backward transposes its operands once and uses the
+// K-contiguous path; this form serves the stand-alone gradient entry points.)
+template <int R, int KB>
 struct ROperand {
-  static constexpr int NI = R / 32;
   static constexpr int CPR = R / 8;
   static constexpr int RPI = 64 / CPR;
+  static constexpr int NI = KB / (4 * RPI);
   int col[NI];     // per lane: global column of its chunk (clamped)
   int krl[NI];     // per lane: k-row within the slab
 
@@ -190,17 +205,15 @@ struct ROperand {
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x4_t ld_tr2(const Q3L_LDS char* p, int second) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Q3L_LDS i16x4_t*)(p));
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Q3L_LDS i16x4_t*)(p + second));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+}
 
 __device__ inline u32x4_t ld_lds16(const Q3L_LDS char* p) {
   return *reinterpret_cast<const Q3L_LDS u32x4_t*>(p);
-}
-__device__ inline u32x4_t ld_tr2(const Q3L_LDS char* p, int second) {
-  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (Q3L_LDS i16x4_t*)(p));
-  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (Q3L_LDS i16x4_t*)(p + second));
-  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
-  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
 }
 
 // ---- tile order -----------------------------------------------------------
@@ -227,24 +240,24 @@ __device__ inline float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f +
 __device__ inline float silu_f(float g) { return g * sigmoid_f(g); }
 
 // ---- fragment readers -----------------------------------------------------
-// K-contiguous tile [rows][64]: lane reads row wb + 32*i + lane%32, k-chunk
-// 2*kk + lane/32 (swizzled).  Addresses: lane base + per-kk offset + 4 KiB*i.
-template <int TT>
+// K-contiguous tile [rows][KB]: lane reads row wb + 32*i + lane%32, k-chunk
+// 2*kk + lane/32 (swizzled).  Addresses: lane base + per-kk offset + i*32 rows.
+template <int TT, int KB>
 struct KFrag {
   uint32_t base;
-  uint32_t koff[4];
+  uint32_t koff[KB / 16];
   __device__ void init(int wb, int lane) {
-    const int r = wb + (lane & 31), h = lane >> 5, sw = ((lane & 31) >> 1) & 7;
-    base = (uint32_t)r * 128u;
+    const int r = wb + (lane & 31), h = lane >> 5, sw = kswz<KB>(lane & 31);
+    base = (uint32_t)r * (2 * KB);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) koff[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
+    for (int kk = 0; kk < KB / 16; ++kk) koff[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
   }
   __device__ void read(const Q3L_LDS char* t, int kk, u32x4_t f[TT]) const {
 #pragma unroll
-    for (int i = 0; i < TT; ++i) f[i] = ld_lds16(t + base + koff[kk] + 4096 * i);
+    for (int i = 0; i < TT; ++i) f[i] = ld_lds16(t + base + koff[kk] + 64 * KB * i);
   }
 };
-// Row-contiguous tile [64][R] (row stride 2R bytes), transposed reads: in
+// Row-contiguous tile [KB][R] (row stride 2R bytes), transposed reads: in
 // 16-lane group g, lane s points at k-row 8*(g/2) + s/4 (+4 for the second
 // read), columns wb + 32*i + 16*(g%2) + 4*(s%4) .. +3 (chunks swizzled by
 // 4 * (k-row & 3)).
@@ -266,24 +279,31 @@ struct RFrag {
   }
 };
 
-template <int ROWS, int TT, bool KC> struct OpSel;
-template <int ROWS, int TT> struct OpSel<ROWS, TT, true> {
-  KOperand<ROWS> ld;
-  KFrag<TT> fr;
+template <int ROWS, int TT, int KB, bool KC> struct OpSel;
+template <int ROWS, int TT, int KB> struct OpSel<ROWS, TT, KB, true> {
+  KOperand<ROWS, KB> ld;
+  KFrag<TT, KB> fr;
 };
-template <int ROWS, int TT> struct OpSel<ROWS, TT, false> {
-  ROperand<ROWS> ld;
+template <int ROWS, int TT, int KB> struct OpSel<ROWS, TT, KB, false> {
+  ROperand<ROWS, KB> ld;
   RFrag<TT, ROWS> fr;
 };
 
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---- the kernel -----------------------------------------------------------
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+// NS LDS stages of KB-deep slabs: slab kt+NS-1 is requested while slab kt is
+// multiplied, so global latency is hidden behind NS-1 slabs of MFMA work.
+template <int BM, int BN, int KB, int NS, bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
+  constexpr int ABYTES = BM * KB * 2, BBYTES = BN * KB * 2;
   constexpr int STAGE = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -294,8 +314,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   map_tile(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  OpSel<BM, TM, AK> oa;
-  OpSel<BN, TN, BKC> ob;
+  OpSel<BM, TM, KB, AK> oa;
+  OpSel<BN, TN, KB, BKC> ob;
+  constexpr int LOADS = decltype(oa.ld)::NI + decltype(ob.ld)::NI;  // per slab
   oa.ld.init(g.a, m0, wave, lane);
   ob.ld.init(g.b, n0, wave, lane);
   oa.fr.init(wm * WM, lane);
@@ -309,31 +330,73 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = (g.K + BK - 1) / BK;
-  oa.ld.issue(g.a, 0, g.K, lds, wave);
-  ob.ld.issue(g.b, 0, g.K, lds + ABYTES, wave);
-  for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads of slab kt are done; the barrier makes every wave's
-    // visible and guarantees slab kt-1 (in the other stage) is fully read.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) {
-      Q3L_LDS char* nx = lds + ((kt + 1) & 1) * STAGE;
-      oa.ld.issue(g.a, (kt + 1) * BK, g.K, nx, wave);
-      ob.ld.issue(g.b, (kt + 1) * BK, g.K, nx + ABYTES, wave);
-    }
-    const Q3L_LDS char* As = lds + (kt & 1) * STAGE;
-    const Q3L_LDS char* Bs = As + ABYTES;
+  const int nk = (g.K + KB - 1) / KB;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4_t af[TM], bfr[TN];
-      oa.fr.read(As, kk, af);
-      ob.fr.read(Bs, kk, bfr);
+  for (int s = 0; s < NS - 1; ++s) {
+    if (s < nk) {
+      oa.ld.issue(g.a, s * KB, g.K, lds + s * STAGE, wave);
+      ob.ld.issue(g.b, s * KB, g.K, lds + s * STAGE + ABYTES, wave);
+    }
+  }
+
+  int cur = 0;                 // stage holding slab kt
+  int nxt = NS - 1;            // stage for slab kt + NS - 1
+  for (int kt = 0; kt < nk; ++kt) {
+    // Slab kt's loads (this wave's) are done once at most the loads of the
+    // NS-2 later slabs are outstanding; the barrier makes all waves' loads
+    // visible and guarantees every wave finished reading the stage about to
+    // be refilled.
+    if (kt + NS - 2 < nk) wait_vmcnt<LOADS * (NS - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + NS - 1 < nk) {
+      Q3L_LDS char* nx = lds + nxt * STAGE;
+      oa.ld.issue(g.a, (kt + NS - 1) * KB, g.K, nx, wave);
+      ob.ld.issue(g.b, (kt + NS - 1) * KB, g.K, nx + ABYTES, wave);
+    }
+    const Q3L_LDS char* As = lds + cur * STAGE;
+    const Q3L_LDS char* Bs = As + ABYTES;
+    // Fragments are double-buffered in registers: the reads for step kk+1
+    // are in flight while the matrix cores work on step kk.
+    u32x4_t af[2][TM], bfr[2][TN];
+    oa.fr.read(As, 0, af[0]);
+    ob.fr.read(Bs, 0, bfr[0]);
+#pragma unroll
+    for (int kk = 0; kk < KB / 16; ++kk) {
+      if (kk + 1 < KB / 16) {
+        oa.fr.read(As, kk + 1, af[(kk + 1) & 1]);
+        ob.fr.read(Bs, kk + 1, bfr[(kk + 1) & 1]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma32(bfr[kk & 1][j], af[kk & 1][i], acc[i][j]);
     }
+    // Instruction order for the slab (scheduling groups): the first step's
+    // fragment reads, then each later step's reads spread evenly over the
+    // matrix instructions of the step before it.  A K-contiguous fragment is
+    // one LDS read, a transposed one two.
+    {
+      constexpr int NR = (AK ? TM : 2 * TM) + (BKC ? TN : 2 * TN);
+      constexpr int NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+      constexpr int RPG = NR / NM > 0 ? NR / NM : 1;   // reads per group
+      constexpr int NG = NR / RPG;
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < KB / 16; ++kk) {
+#pragma unroll
+        for (int r = 0; r < NG; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, RPG, 0);
+        }
+        if (NM - PER * NG > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NG, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
+
+    cur = (cur + 1 == NS) ? 0 : cur + 1;
+    nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
   }
 
   // ---- epilogue: lane holds C[m][n..n+3] for each (i, j, q) ----
@@ -427,39 +490,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC>
+template <int BM, int BN, int KB, int NS, bool AK, bool BKC>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   dim3 grid(ntm * ntn), block(256);
+#define Q3L_GK(E) \
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, KB, NS, AK, BKC, E>), grid, block, 0, s, g)
   switch (g.epi.kind) {
-    case EPI_STORE:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI_STORE>), grid, block, 0, s, g);
-      break;
-    case EPI_PARTIAL:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI_PARTIAL>), grid, block, 0, s, g);
-      break;
-    case EPI_SILU_MUL:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI_SILU_MUL>), grid, block, 0, s, g);
-      break;
-    case EPI_SILU_BWD:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI_SILU_BWD>), grid, block, 0, s, g);
-      break;
-    case EPI_WGRAD:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI_WGRAD>), grid, block, 0, s, g);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case EPI_STORE: Q3L_GK(EPI_STORE); break;
+    case EPI_PARTIAL: Q3L_GK(EPI_PARTIAL); break;
+    case EPI_SILU_MUL: Q3L_GK(EPI_SILU_MUL); break;
+    case EPI_SILU_BWD: Q3L_GK(EPI_SILU_BWD); break;
+    case EPI_WGRAD: Q3L_GK(EPI_WGRAD); break;
+    default: return hipErrorInvalidValue;
   }
+#undef Q3L_GK
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int KB, int NS>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
   const bool ak = g.a.k_contig, bk = g.b.k_contig;
-  if (ak && bk) return launch_epi<BM, BN, true, true>(g, s);
-  if (ak && !bk) return launch_epi<BM, BN, true, false>(g, s);
-  if (!ak && !bk) return launch_epi<BM, BN, false, false>(g, s);
-  return launch_epi<BM, BN, false, true>(g, s);
+  if (ak && bk) return launch_epi<BM, BN, KB, NS, true, true>(g, s);
+  if (ak && !bk) return launch_epi<BM, BN, KB, NS, true, false>(g, s);
+  if (!ak && !bk) return launch_epi<BM, BN, KB, NS, false, false>(g, s);
+  return launch_epi<BM, BN, KB, NS, false, true>(g, s);
 }
 
 }  // namespace
@@ -471,9 +526,9 @@ hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   auto tiles = [&](int bm, int bn) {
     return (int64_t)((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= kCUs) return launch_layout<256, 256>(g, s);
-  if (tiles(256, 128) >= kCUs) return launch_layout<256, 128>(g, s);
-  return launch_layout<128, 128>(g, s);
+  if (tiles(256, 256) >= kCUs) return launch_layout<256, 256, 64, 2>(g, s);
+  if (tiles(256, 128) >= kCUs) return launch_layout<256, 128, 64, 2>(g, s);
+  return launch_layout<128, 128, 64, 2>(g, s);
 }
 
 }  // namespace q3l

@@ -66,6 +66,11 @@ hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Plain fp32 GEMM with the same argument structure (correctness path).
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
 
+// bf16 dst[c][r] = src[r][c] (r < rows, c < cols); dst columns r in
+// [rows, rows_pad) are zero.  rows_pad and cols multiples of 8.
+hipError_t transpose_bf16(int rows, int rows_pad, int cols, const void* src,
+                          int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s);
+
 // ---- norms / RoPE / elementwise (dtype: 0 fp32, 1 bf16) -------------------
 hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
                        const void* w, float eps, void* y, float* rstd,
@@ -101,9 +106,6 @@ hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
                            float* wq_part, float* wk_part, int* nparts,
                            hipStream_t s);
 int qknorm_bwd_max_parts();
-// Elementwise conversions used by the correctness path.
-hipError_t add_f32_to(int dtype, int64_t n, const float* a, void* out,
-                      hipStream_t s);
 
 // ---- attention ------------------------------------------------------------
 struct AttnArgs {
