@@ -30,6 +30,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int KT = 64;        // keys per tile
+constexpr float kTau = 8.0f;  // rescale threshold (log2 units), see the forward
 constexpr int KTP = KT + 8;   // padded row length of a transposed tile
 
 struct FwdP {
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = s[c][e] * p.scale_log2;
+          float v = s[c][e];
           if (need_mask) {
             const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
             if (kv > qrow || kv >= L) v = -INFINITY;
@@ -183,25 +184,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
           s[c][e] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
+      // The reference maximum m_run moves (and O, l are rescaled) only when a
+      // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
+      // the result is exact, and the 64-multiply rescale is usually skipped.
+      if (__any(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      }
+      const float neg = -m_run;
       float rs = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pv = exp2f(s[c][e] - m_new);
+          const float pv = exp2f(fmaf(s[c][e], p.scale_log2, neg));
           s[c][e] = pv;
           rs += pv;
         }
       rs += __shfl_xor(rs, 32, 64);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      l_run += rs;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4_t pf = pack_half(s[ks >> 1], ks & 1);
@@ -263,7 +271,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
   // Per stage: Q [QT][DHP], Q^T [DH][QT+8], dO [QT][DHP], dO^T [DH][QT+8].
   constexpr int STAGE = 2 * QT * DHP + 2 * DH * (QT + 8);
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][STAGE];
-  __shared__ float sL[2][QT], sD[2][QT];
+  __shared__ __attribute__((aligned(16))) float sL[2][QT];
+  __shared__ __attribute__((aligned(16))) float sD[2][QT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -364,17 +373,27 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
           dp[c] = mfma32(ld16(sO + off), vf[kk], dp[c]);
         }
       }
-      // lane: key mykv; rows q = q0 + 32c + 8(e/4) + 4h + e%4
+      // lane: key mykv; rows q = q0 + 32c + 8(e/4) + 4h + e%4 -- four
+      // consecutive rows per (c, e/4), so LSE and delta come in float4s.
+      const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > L) || (kw0 + 32 > L);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qi = 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-          const int q = q0 + qi;
-          float pv = exp2f(s[c][e] * p.scale_log2 - sL[buf][qi]);
-          if (mykv > q || q >= L || mykv >= L) pv = 0.f;
-          s[c][e] = pv;
-          dp[c][e] = pv * (dp[c][e] - sD[buf][qi]);
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int qb = 32 * c + 8 * e4 + 4 * h;
+          const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sL[buf][qb]);
+          const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][qb]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * e4 + r;
+            float pv = exp2f(fmaf(s[c][e], p.scale_log2, -lq[r]));
+            if (need_mask) {
+              const int q = q0 + qb + r;
+              if (mykv > q || q >= L || mykv >= L) pv = 0.f;
+            }
+            s[c][e] = pv;
+            dp[c][e] = pv * (dp[c][e] - dq4[r]);
+          }
         }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -523,13 +542,16 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
           dp[c] = mfma32(ld16(sV + off), of[kk], dp[c]);
         }
       }
+      const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-          float pv = exp2f(s[c][e] * p.scale_log2 - lse2);
-          if (kv > qrow || kv >= L) pv = 0.f;
+          float pv = exp2f(fmaf(s[c][e], p.scale_log2, -lse2));
+          if (need_mask) {
+            const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (kv > qrow || kv >= L) pv = 0.f;
+          }
           dp[c][e] = pv * (dp[c][e] - dlt);
         }
 #pragma unroll

@@ -19,15 +19,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __host__ __device__ inline float bf2f(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
-// Round to nearest, ties to even (inputs are finite).
-__host__ __device__ inline bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+// fp32 -> bf16, round to nearest (ties to even): one v_cvt_pk_bf16_f32 per
+// pair of values on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
-__host__ __device__ inline uint32_t pack2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) |
-         (static_cast<uint32_t>(f2bf(hi)) << 16);
+__device__ inline bf16_t f2bf(float f) {
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 __host__ __device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __host__ __device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
