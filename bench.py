@@ -34,6 +34,17 @@ METRIC = ("decoder-layer fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), "
           "1 MI355X")
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
+
+# HBM traffic of the dominant kernel from two hardware-counter passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over `bench.py
+# --kernel-probe`, each scaled by what the same counter reads for the 1 GiB
+# calibration copy.  Valid only for the kernel source it was taken on: the
+# digest below is of gemm_bf16.hip, and a changed source reports null.
+TRAFFIC = {"source_sha256": "ab5ec2d82185957b",
+           "fetch_kib": 1192143.2, "write_kib": 1169351.1,
+           "copy_fetch_kib": 524302.25, "copy_write_kib": 1048576.0,
+           "bytes": 3638858458}
 
 WORKLOADS = {
     "qwen3-8b-bf16-fwd-bwd": 4,
@@ -104,26 +115,79 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Dominant kernel: the fused gate/up + SwiGLU GEMM, same shapes as in the
-    # layer, timed with HIP events on the launch stream.
-    T = lc.T
-    hn = torch.randn((T, lc.d), device=dev).to(bf)
-    f = torch.empty((T, lc.d_ffn), dtype=bf, device=dev)
-    gu = torch.empty((T, 2 * lc.d_ffn), dtype=bf, device=dev)
-    reps = max(10, steps)
+    k_ms = time_dominant(lc, W["gate"], W["up"], stream, max(10, steps))
+    del saved
+    return {"elapsed": elapsed, "kernel_ms": k_ms}
+
+
+def dominant_operands(lc, gate, up):
+    import torch
+    bf = torch.bfloat16
+    gen = torch.Generator(device=gate.device).manual_seed(7)
+    hn = torch.randn((lc.T, lc.d), device=gate.device, generator=gen).to(bf)
+    f = torch.empty((lc.T, lc.d_ffn), dtype=bf, device=gate.device)
+    gu = torch.empty((lc.T, 2 * lc.d_ffn), dtype=bf, device=gate.device)
+    return hn, f, gu
+
+
+def time_dominant(lc, gate, up, stream, reps: int) -> float:
+    """Average duration (ms) of the fused gate/up GEMM + SwiGLU kernel at the
+    layer's shapes, with HIP events recorded on the stream it launches on."""
+    import torch
+    import qwen3_decoder_layer_amd as q3
+    hn, f, gu = dominant_operands(lc, gate, up)
     for _ in range(3):
-        q3.swiglu_fwd(hn, W["gate"], W["up"], f=f, gu=gu, stream=stream)
+        q3.swiglu_fwd(hn, gate, up, f=f, gu=gu, stream=stream)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(reps):
-        q3.swiglu_fwd(hn, W["gate"], W["up"], f=f, gu=gu, stream=stream)
+        q3.swiglu_fwd(hn, gate, up, f=f, gu=gu, stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
-    k_ms = ev0.elapsed_time(ev1) / reps
-    del saved
-    return {"elapsed": elapsed, "kernel_ms": k_ms,
-            "kernel_flops": 2.0 * T * lc.d * 2 * lc.d_ffn}
+    return ev0.elapsed_time(ev1) / reps
+
+
+def dominant_work(T: int, d: int, f: int) -> tuple:
+    """(FLOPs, algorithmic HBM bytes) of one gate/up + SwiGLU launch (bf16):
+    2*T*d*(2f) multiply-adds; read hn and both weights once, write f and the
+    saved g|u once."""
+    return 2 * T * d * 2 * f, 2 * (T * d + 2 * f * d + T * f + 2 * T * f)
+
+
+def kernel_probe(cfg: dict) -> None:
+    """Short run for hardware-counter passes: a plain 1 GiB device copy (the
+    calibration kernel: reads and writes exactly COPY_BYTES), then the
+    dominant kernel, each a few times."""
+    import torch
+    import qwen3_decoder_layer_amd as q3
+    lc = q3.LayerConfig.from_dict(cfg)
+    dev = "cuda"
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    gen = torch.Generator(device=dev).manual_seed(3)
+    gate = (0.02 * torch.randn((lc.d_ffn, lc.d), device=dev, generator=gen)).to(torch.bfloat16)
+    up = (0.02 * torch.randn((lc.d_ffn, lc.d), device=dev, generator=gen)).to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    ms = time_dominant(lc, gate, up, stream, 5)
+    torch.cuda.synchronize()
+    print(f"kernel probe: copy {COPY_BYTES} B x3, dominant kernel {ms:.3f} ms avg",
+          flush=True)
+
+
+def traffic_bytes():
+    """Measured HBM bytes per dominant-kernel launch, or None when no counter
+    pass exists for the current kernel source."""
+    if TRAFFIC is None:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "qwen3_decoder_layer_amd", "csrc", "gemm_bf16.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != TRAFFIC["source_sha256"]:
+        return None
+    return TRAFFIC["bytes"]
 
 
 def cpu_baseline(cfg: dict, budget_tokens: int) -> dict:
@@ -162,20 +226,27 @@ def main():
     ap.add_argument("--workload", default="qwen3-8b-bf16-fwd-bwd",
                     choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--kernel-probe", action="store_true",
+                    help="only the calibration copy and the dominant kernel "
+                         "(for hardware-counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
               "supported (the layer's local compute runs on a single device).",
               file=sys.stderr)
         sys.exit(2)
+    if args.kernel_probe:
+        kernel_probe(synth.preset(WORKLOADS[args.workload]))
+        return
     cfg, inp = synth.preset_inputs(WORKLOADS[args.workload])
     res = gpu_run(cfg, inp, args.steps, args.warmup)
     fl = model_flops(cfg, cfg["backward"])
     T = cfg["B"] * cfg["L"]
     ms = res["elapsed"] / args.steps * 1e3
     tflops = fl["total"] / (ms * 1e-3) / 1e12
-    k_tflops = res["kernel_flops"] / (res["kernel_ms"] * 1e-3) / 1e12
+    k_flops, k_bytes = dominant_work(T, cfg["d"], cfg["d_ffn"])
+    k_tflops = k_flops / (res["kernel_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -203,7 +274,9 @@ def main():
                      "bound": "mfma", "achieved": k_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": k_tflops / PEAK_BF16_TFLOPS,
-                     "avg_ms": res["kernel_ms"], "traffic": None},
+                     "avg_ms": res["kernel_ms"],
+                     "algorithmic_bytes": k_bytes,
+                     "traffic": traffic_bytes()},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

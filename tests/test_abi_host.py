@@ -1,0 +1,183 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/q3layer.h declares, and
+turn bad arguments into a status plus a message before any launch.  Nothing
+here enqueues device work: every call either is pure host arithmetic
+(sizes, layouts) or fails validation first.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q3layer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    names = re.findall(r"\b(q3l_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from qwen3_decoder_layer_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.skip("libq3layer.so is not built (run __graft_entry__.build())")
+    return _abi
+
+
+@pytest.fixture(scope="module")
+def lib(abi):
+    return abi.load()
+
+
+def test_header_declares_the_layer_calls():
+    names = declared_functions()
+    for n in ("q3l_validate", "q3l_saved_bytes", "q3l_workspace_bytes",
+              "q3l_layer_forward", "q3l_layer_backward", "q3l_last_error"):
+        assert n in names
+    assert len(names) >= 15
+
+
+def test_every_declared_symbol_is_exported(abi):
+    raw = C.CDLL(abi.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_binding_mirrors_every_declaration(abi):
+    # The ctypes layer restates each prototype; nothing declared is unbound.
+    assert set(declared_functions()) <= set(abi.PROTOTYPES)
+
+
+def err(lib) -> str:
+    return (lib.q3l_last_error() or b"").decode()
+
+
+def cfg_of(abi, **kw):
+    base = dict(d=512, h_q=8, h_kv=4, d_h=64, d_ffn=1024, B=2, L=64, eps=1e-6,
+                rope_theta=1e6, qk_norm=1, tp_partial=0, dtype=abi.Q3L_BF16)
+    base.update(kw)
+    return abi.Cfg(**base)
+
+
+def test_validate_accepts_the_workload_shapes(abi, lib):
+    import synth
+    for i in range(len(synth.CONFIGS)):
+        c = synth.preset(i)
+        cfg = cfg_of(abi, d=c["d"], h_q=c["h_q"], h_kv=c["h_kv"], d_h=c["d_h"],
+                     d_ffn=c["d_ffn"], B=c["B"], L=c["L"],
+                     tp_partial=int(c.get("tp_partial", 0)),
+                     dtype=abi.Q3L_BF16 if c["dtype"] == "bf16" else abi.Q3L_F32)
+        assert lib.q3l_validate(C.byref(cfg)) == 0, err(lib)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("h_kv", 3, 1),          # h_q % h_kv != 0
+    ("d_h", 96, 2),          # unsupported head dim
+    ("d", 0, 1),             # non-positive size
+    ("d", 516, 2),           # not a multiple of 8
+    ("d_ffn", 1020, 2),
+    ("d", 16384, 2),         # beyond the supported width
+    ("eps", 0.0, 1),
+    ("eps", float("inf"), 1),
+    ("rope_theta", -1.0, 1),
+    ("qk_norm", 2, 1),
+    ("dtype", 7, 1),
+    ("L", -1, 1),
+])
+def test_validate_rejects(abi, lib, field, value, status):
+    cfg = cfg_of(abi, **{field: value})
+    assert lib.q3l_validate(C.byref(cfg)) == status
+    assert len(err(lib)) > 5
+
+
+def test_validate_null_cfg(abi, lib):
+    assert lib.q3l_validate(None) == 1
+
+
+def test_saved_layout_is_ordered_and_aligned(abi, lib):
+    for dtype in (abi.Q3L_F32, abi.Q3L_BF16):
+        cfg = cfg_of(abi, B=3, L=129, dtype=dtype)
+        lay = abi.SavedLayout()
+        assert lib.q3l_saved_layout_of(C.byref(cfg), C.byref(lay)) == 0
+        offs = [getattr(lay, n) for n in abi.SAVED_FIELDS]
+        assert all(o % 256 == 0 for o in offs)
+        assert offs == sorted(offs)
+        assert lib.q3l_saved_bytes(C.byref(cfg)) == lay.total
+        T, es = 3 * 129, 4 if dtype == abi.Q3L_F32 else 2
+        # The saved block holds at least the activations the backward reads.
+        assert lay.total >= T * (2 * 512 + 2 * 512 + 3 * 1024) * es
+
+
+def test_workspace_grows_with_backward(abi, lib):
+    cfg = cfg_of(abi)
+    assert lib.q3l_workspace_bytes(C.byref(cfg), 1) >= \
+        lib.q3l_workspace_bytes(C.byref(cfg), 0)
+
+
+def test_forward_rejects_null_and_misaligned_pointers_before_launch(abi, lib):
+    cfg = cfg_of(abi)
+    buf = C.create_string_buffer(4096)
+    base = (C.addressof(buf) + 255) // 256 * 256
+    w = abi.Weights(**{n: base for n in abi.PARAMS})
+    out = abi.Outputs(y=base)
+    # x NULL
+    st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), None, C.byref(out),
+                               None, None, 0, None)
+    assert st == 1 and "x" in err(lib)
+    # a misaligned weight
+    w.gate = base + 2
+    st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, C.byref(out),
+                               None, None, 0, None)
+    assert st == 3 and "gate" in err(lib)
+    # NULL weights struct / outputs
+    assert lib.q3l_layer_forward(C.byref(cfg), None, base, C.byref(out),
+                                 None, None, 0, None) == 1
+    w.gate = base
+    assert lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, None,
+                                 None, None, 0, None) == 1
+
+
+def test_backward_rejects_bad_flags_and_small_workspace(abi, lib):
+    cfg = cfg_of(abi)
+    buf = C.create_string_buffer(4096)
+    base = (C.addressof(buf) + 255) // 256 * 256
+    w = abi.Weights(**{n: base for n in abi.PARAMS})
+    g = abi.Grads(**{n: base for n in abi.PARAMS})
+    st = lib.q3l_layer_backward(C.byref(cfg), C.byref(w), base, base, base, base,
+                                C.byref(g), 64, base, 1 << 40, None)
+    assert st == 1 and "flag" in err(lib)
+    st = lib.q3l_layer_backward(C.byref(cfg), C.byref(w), base, base, base, base,
+                                C.byref(g), abi.BWD_INPUT | abi.BWD_WEIGHT,
+                                base, 16, None)
+    assert st == 1 and "workspace" in err(lib)
+    tp = cfg_of(abi, tp_partial=1)
+    st = lib.q3l_layer_backward(C.byref(tp), C.byref(w), base, base, base, base,
+                                C.byref(g), abi.BWD_INPUT, base, 1 << 40, None)
+    assert st == 2
+
+
+def test_phase_entry_points_validate(abi, lib):
+    # M, N, K rules of the linear entry points and head-dim rule of attention.
+    st = lib.q3l_linear_fwd(abi.Q3L_BF16, 16, 12, 16, None, None, None, None,
+                            None)
+    assert st == 1
+    st = lib.q3l_attention_fwd(abi.Q3L_BF16, 1, 16, 4, 2, 80, None, 0, None, 0,
+                               None, 0, None, 0, None, None)
+    assert st == 2
+
+
+def test_version_and_missing_library_fails_loudly(abi, lib, monkeypatch):
+    assert lib.q3l_version() >= 1
+    # No fallback: without the built library the binding raises.
+    monkeypatch.setattr(abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        abi.load("/nonexistent/libq3layer.so")
