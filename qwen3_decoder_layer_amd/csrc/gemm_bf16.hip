@@ -53,21 +53,14 @@ __device__ inline uint64_t uni64(uint64_t v) {
 
 // 16 bytes per lane from a raw buffer straight into LDS: lane i's data lands
 // at LDS byte lds_base + 16 * i.  The buffer covers [p, p + 2 GiB) with
-// stride 0, so `voff` is a byte offset and any offset >= 2^31 reads zeros.
-// Issued as inline asm: the compiler then does not treat the pending LDS
-// writes as aliasing every LDS read of the current slab (it would otherwise
-// wait for the next slab's loads before reading this one).  The kernel waits
-// for these loads itself (s_waitcnt vmcnt(0) before each slab's barrier).
-typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
-__device__ inline void dma16(uint64_t p, uint32_t voff, uint32_t lds_base) {
-  const u32x4s_t rsrc = {(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu,
-                         0x00020000u};
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(lds_base)
-      : "memory", "m0");
+// stride 0, so `voff + soff` (per-lane + uniform) is a byte offset and any
+// offset >= 2^31 reads zeros.  The kernel orders these writes against its
+// LDS reads itself: an explicit s_waitcnt vmcnt before each stage barrier.
+__device__ inline void dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16,
+                                           voff, soff, 0, 0);
 }
 __device__ inline uint32_t lds_addr(const Q3L_LDS char* p) {
   return (uint32_t)(uintptr_t)p;
@@ -104,22 +97,22 @@ __device__ inline int kswz(int row) {
   return KB == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
-template <int R, int KB>
+template <int R, int KB, int NW>
 struct KOperand {
   static constexpr int CPRK = KB / 8;
   static constexpr int RPW = 64 / CPRK;
-  static constexpr int NI = R / (4 * RPW);   // wave-instructions per thread per slab
-  uint32_t voff[NI];   // per lane: byte offset of its chunk at k = 0
-  int kel[NI];         // per lane: first k (elements) of its chunk at k0 = 0
+  static constexpr int NI = R / (NW * RPW);  // wave-instructions per thread per slab
+  uint32_t voff[NI];   // per lane: byte offset of its chunk at k0 = 0
+  uint32_t vtail[NI];  // the same for the last slab: kOOB where the chunk is past K
   uint64_t base[NI];   // uniform: segment base of the instruction's rows
 
-  __device__ void init(const Operand& o, int r0, int wave, int lane) {
+  __device__ void init(const Operand& o, int r0, int K, int wave, int lane) {
+    const int klast = (K - 1) / KB * KB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = 4 * i + wave;
+      const int q = NW * i + wave;
       const int row = RPW * q + lane / CPRK;
       const int c = (lane % CPRK) ^ kswz<KB>(row);
-      kel[i] = 8 * c;
       int gr = r0 + row;
       uint64_t p;
       int64_t ld;
@@ -142,17 +135,18 @@ struct KOperand {
         if (gr > o.rows - 1) gr = o.rows - 1;
         voff[i] = (uint32_t)((int64_t)(gr - st) * ld * 2 + 16 * c);
       }
+      vtail[i] = (klast + 8 * c < K) ? voff[i] : kOOB;
       base[i] = p;
     }
   }
-  // Issue the slab starting at k0 into LDS stage `dst` (R * KB * 2 bytes).
-  __device__ void issue(const Operand&, int k0, int K, Q3L_LDS char* dst,
-                        int wave) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t off = (k0 + kel[i] < K) ? voff[i] + 2u * (uint32_t)k0 : kOOB;
-      dma16(base[i], off, uni(lds_addr(dst + 1024 * (4 * i + wave))));
-    }
+  // Wave-instruction i of the slab starting at k0, into LDS stage `dst`
+  // (R * KB * 2 bytes); `last` (uniform) selects the offsets that zero-fill
+  // chunks past K.  No per-slab address arithmetic: the slab offset rides in
+  // the scalar offset.
+  __device__ void issue_one(const Operand&, int i, int k0, int, bool last,
+                            Q3L_LDS char* dst, int wave) const {
+    dma16(base[i], last ? vtail[i] : voff[i], uni(2u * (uint32_t)k0),
+          uni(lds_addr(dst + 1024 * (NW * i + wave))));
   }
 };
 
@@ -165,18 +159,18 @@ struct KOperand {
 // transposing LDS read.  (It runs at roughly a third of ds_read_b128's byte
 // rate, so the layer's backward transposes its operands once and uses the
 // K-contiguous path; this form serves the stand-alone gradient entry points.)
-template <int R, int KB>
+template <int R, int KB, int NW>
 struct ROperand {
   static constexpr int CPR = R / 8;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int NI = KB / (4 * RPI);
+  static constexpr int NI = KB / (NW * RPI);
   int col[NI];     // per lane: global column of its chunk (clamped)
   int krl[NI];     // per lane: k-row within the slab
 
-  __device__ void init(const Operand& o, int r0, int wave, int lane) {
+  __device__ void init(const Operand& o, int r0, int, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = 4 * i + wave;
+      const int q = NW * i + wave;
       const int kr = RPI * q + lane / CPR;
       const int c = (lane % CPR) ^ (4 * (kr & 3));
       int n = r0 + 8 * c;
@@ -185,22 +179,19 @@ struct ROperand {
       krl[i] = kr;
     }
   }
-  __device__ void issue(const Operand& o, int k0, int K, Q3L_LDS char* dst,
-                        int wave) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int q = 4 * i + wave;
-      int kq = k0 + RPI * q;                    // uniform first k-row
-      if (kq > K - 1) kq = K - 1;
-      uint64_t p;
-      int64_t ld;
-      int st;
-      pick(o, kq, p, ld, st);
-      const int k = k0 + krl[i];
-      const uint32_t off =
-          k < K ? (uint32_t)(((int64_t)(k - st) * ld + col[i]) * 2) : kOOB;
-      dma16(p, off, uni(lds_addr(dst + 1024 * (4 * i + wave))));
-    }
+  __device__ void issue_one(const Operand& o, int i, int k0, int K, bool,
+                            Q3L_LDS char* dst, int wave) const {
+    const int q = NW * i + wave;
+    int kq = k0 + RPI * q;                    // uniform first k-row
+    if (kq > K - 1) kq = K - 1;
+    uint64_t p;
+    int64_t ld;
+    int st;
+    pick(o, kq, p, ld, st);
+    const int k = k0 + krl[i];
+    const uint32_t off =
+        k < K ? (uint32_t)(((int64_t)(k - st) * ld + col[i]) * 2) : kOOB;
+    dma16(p, off, 0u, uni(lds_addr(dst + 1024 * (NW * i + wave))));
   }
 };
 
@@ -252,9 +243,8 @@ struct KFrag {
 #pragma unroll
     for (int kk = 0; kk < KB / 16; ++kk) koff[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
   }
-  __device__ void read(const Q3L_LDS char* t, int kk, u32x4_t f[TT]) const {
-#pragma unroll
-    for (int i = 0; i < TT; ++i) f[i] = ld_lds16(t + base + koff[kk] + 64 * KB * i);
+  __device__ u32x4_t read(const Q3L_LDS char* t, int kk, int i) const {
+    return ld_lds16(t + base + koff[kk] + 64 * KB * i);
   }
 };
 // Row-contiguous tile [KB][R] (row stride 2R bytes), transposed reads: in
@@ -273,19 +263,18 @@ struct RFrag {
       base[i] = rowoff + (uint32_t)chunk * 16u;
     }
   }
-  __device__ void read(const Q3L_LDS char* t, int kk, u32x4_t f[TT]) const {
-#pragma unroll
-    for (int i = 0; i < TT; ++i) f[i] = ld_tr2(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
+  __device__ u32x4_t read(const Q3L_LDS char* t, int kk, int i) const {
+    return ld_tr2(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
   }
 };
 
-template <int ROWS, int TT, int KB, bool KC> struct OpSel;
-template <int ROWS, int TT, int KB> struct OpSel<ROWS, TT, KB, true> {
-  KOperand<ROWS, KB> ld;
+template <int ROWS, int TT, int KB, int NW, bool KC> struct OpSel;
+template <int ROWS, int TT, int KB, int NW> struct OpSel<ROWS, TT, KB, NW, true> {
+  KOperand<ROWS, KB, NW> ld;
   KFrag<TT, KB> fr;
 };
-template <int ROWS, int TT, int KB> struct OpSel<ROWS, TT, KB, false> {
-  ROperand<ROWS, KB> ld;
+template <int ROWS, int TT, int KB, int NW> struct OpSel<ROWS, TT, KB, NW, false> {
+  ROperand<ROWS, KB, NW> ld;
   RFrag<TT, ROWS> fr;
 };
 
@@ -293,13 +282,38 @@ template <int N>
 __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Workgroup barrier for the LDS stages: this wave's LDS reads have returned
+// (so a stage it read may be refilled once everyone is past), without the
+// vmcnt(0) a fenced __syncthreads() would add -- younger slabs' requests
+// stay in flight.  The memory clobber keeps LDS accesses on their side.
+__device__ inline void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Scheduling groups for one k-step of NM matrix instructions: the NR LDS
+// fragment reads of the next step go out early (one after each of the first
+// matrix instructions, or spread evenly when there are more reads than
+// matrix instructions), and the NV global->LDS requests are spread evenly,
+// so the address FIFO never backs up into the matrix-instruction stream.
+template <int R, int NM, int NR, int NV>
+__device__ inline void sched_from() {
+  if constexpr (R < NM) {
+    constexpr int rd = NR > NM ? ((R + 1) * NR) / NM - (R * NR) / NM : (R < NR ? 1 : 0);
+    constexpr int vm = ((R + 1) * NV) / NM - (R * NV) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, rd, 0);
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);
+    sched_from<R + 1, NM, NR, NV>();
+  }
+}
 
 // ---- the kernel -----------------------------------------------------------
 // NS LDS stages of KB-deep slabs: slab kt+NS-1 is requested while slab kt is
 // multiplied, so global latency is hidden behind NS-1 slabs of MFMA work.
-template <int BM, int BN, int KB, int NS, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
+  constexpr int WGN = NW / 2;                  // waves along N (2 along M)
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int ABYTES = BM * KB * 2, BBYTES = BN * KB * 2;
   constexpr int STAGE = ABYTES + BBYTES;
@@ -308,17 +322,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   int tm, tn;
   map_tile(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  OpSel<BM, TM, KB, AK> oa;
-  OpSel<BN, TN, KB, BKC> ob;
+  OpSel<BM, TM, KB, NW, AK> oa;
+  OpSel<BN, TN, KB, NW, BKC> ob;
   constexpr int LOADS = decltype(oa.ld)::NI + decltype(ob.ld)::NI;  // per slab
-  oa.ld.init(g.a, m0, wave, lane);
-  ob.ld.init(g.b, n0, wave, lane);
+  oa.ld.init(g.a, m0, g.K, wave, lane);
+  ob.ld.init(g.b, n0, g.K, wave, lane);
   oa.fr.init(wm * WM, lane);
   ob.fr.init(wn * WN, lane);
 
@@ -330,74 +344,111 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  constexpr int KS = KB / 16;                  // k-steps per slab
+  static_assert(KS % 2 == 0 && NS >= 2, "slab pipeline shape");
+  // A slab's requests are spread over SP k-steps: with three or more stages
+  // over a whole slab's worth of steps, with two (no slack) all at once.
+  constexpr int SP = NS >= 3 ? KS : 1;
+  constexpr int NIA = decltype(oa.ld)::NI;
+  static_assert(LOADS % SP == 0, "requests split evenly over the steps");
+  constexpr int NV = LOADS / SP;               // requests per k-step
   const int nk = (g.K + KB - 1) / KB;
+  const int klast = nk - 1;
+  // Part `part` (of SP) of slab kt's requests into stage dst.
+  auto issue_part = [&](int kt, Q3L_LDS char* dst, int part) {
+    const bool last = kt == klast;
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) {
-    if (s < nk) {
-      oa.ld.issue(g.a, s * KB, g.K, lds + s * STAGE, wave);
-      ob.ld.issue(g.b, s * KB, g.K, lds + s * STAGE + ABYTES, wave);
+    for (int q = 0; q < LOADS; ++q) {
+      if (q / NV != part) continue;
+      if (q < NIA)
+        oa.ld.issue_one(g.a, q, kt * KB, g.K, last, dst, wave);
+      else
+        ob.ld.issue_one(g.b, q - NIA, kt * KB, g.K, last, dst + ABYTES, wave);
     }
-  }
+  };
+  // Fragment reads in the order the matrix instructions consume them
+  // (row-major over the TM x TN accumulators): a0, b0 .. b{TN-1}, a1 ..
+  auto frags = [&](const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk,
+                   u32x4_t (&af)[TM], u32x4_t (&bf)[TN]) {
+    af[0] = oa.fr.read(As, kk, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = ob.fr.read(Bs, kk, j);
+#pragma unroll
+    for (int i = 1; i < TM; ++i) af[i] = oa.fr.read(As, kk, i);
+  };
+  auto mma = [&](const u32x4_t (&af)[TM], const u32x4_t (&bf)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bf[j], af[i], acc[i][j]);
+  };
+  // A K-contiguous fragment is one LDS read, a transposed one two.
+  constexpr int NR = (AK ? TM : 2 * TM) + (BKC ? TN : 2 * TN);
+  constexpr int NM = TM * TN;
 
-  int cur = 0;                 // stage holding slab kt
-  int nxt = NS - 1;            // stage for slab kt + NS - 1
-  for (int kt = 0; kt < nk; ++kt) {
-    // Slab kt's loads (this wave's) are done once at most the loads of the
-    // NS-2 later slabs are outstanding; the barrier makes all waves' loads
-    // visible and guarantees every wave finished reading the stage about to
-    // be refilled.
-    if (kt + NS - 2 < nk) wait_vmcnt<LOADS * (NS - 2)>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + NS - 1 < nk) {
-      Q3L_LDS char* nx = lds + nxt * STAGE;
-      oa.ld.issue(g.a, (kt + NS - 1) * KB, g.K, nx, wave);
-      ob.ld.issue(g.b, (kt + NS - 1) * KB, g.K, nx + ABYTES, wave);
+  // Slab kt lives in stage kt % NS.  All stages start filling at once.
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int part = 0; part < SP; ++part) issue_part(min(st, klast), lds + st * STAGE, part);
+  wait_vmcnt<LOADS * (NS - 1)>();
+  stage_barrier();
+  // Fragments are double-buffered in registers: while the matrix cores work
+  // on k-step kk, the reads for step kk+1 are in flight.
+  u32x4_t af[2][TM], bfr[2][TN];
+  frags(lds, lds + ABYTES, 0, af[0], bfr[0]);
+
+  // The stage barrier sits before the LAST k-step of a slab, whose fragments
+  // are already in registers: after it the next slab's first fragments are
+  // read, and the stage just drained starts receiving slab kt+NS (part 0
+  // now, parts 1.. during the next slab's first steps), all hidden behind
+  // matrix instructions.  Before the barrier a wave waits for its own part
+  // of slab kt+1; NS-2 younger slabs stay in flight.  Requests past the last
+  // slab repeat it into stages nothing reads any more (in the first
+  // iteration the pending parts repeat slab NS-1 into its own stage: the
+  // same bytes).
+  int cur = 0;
+  int pend = min(NS - 1, klast);
+  Q3L_LDS char* pend_dst = lds + (NS - 1) * STAGE;
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const int nxt = cur + 1 == NS ? 0 : cur + 1;
+    Q3L_LDS char* As = lds + cur * STAGE;
+    const Q3L_LDS char* Bs = As + ABYTES;
+#pragma unroll
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      frags(As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+      if (kk + 1 < SP) issue_part(pend, pend_dst, kk + 1);
+      mma(af[kk & 1], bfr[kk & 1]);
+      if (kk + 1 < SP)
+        sched_from<0, NM, NR, NV>();
+      else
+        sched_from<0, NM, NR, 0>();
     }
+    wait_vmcnt<LOADS * (NS - 2)>();
+    stage_barrier();
+    const Q3L_LDS char* Nx = lds + nxt * STAGE;
+    frags(Nx, Nx + ABYTES, 0, af[0], bfr[0]);
+    pend = min(kt + NS, klast);
+    pend_dst = As;
+    issue_part(pend, pend_dst, 0);
+    mma(af[(KS - 1) & 1], bfr[(KS - 1) & 1]);
+    sched_from<0, NM, NR, NV>();
+    cur = nxt;
+  }
+  {
     const Q3L_LDS char* As = lds + cur * STAGE;
     const Q3L_LDS char* Bs = As + ABYTES;
-    // Fragments are double-buffered in registers: the reads for step kk+1
-    // are in flight while the matrix cores work on step kk.
-    u32x4_t af[2][TM], bfr[2][TN];
-    oa.fr.read(As, 0, af[0]);
-    ob.fr.read(Bs, 0, bfr[0]);
 #pragma unroll
-    for (int kk = 0; kk < KB / 16; ++kk) {
-      if (kk + 1 < KB / 16) {
-        oa.fr.read(As, kk + 1, af[(kk + 1) & 1]);
-        ob.fr.read(Bs, kk + 1, bfr[(kk + 1) & 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma32(bfr[kk & 1][j], af[kk & 1][i], acc[i][j]);
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      frags(As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+      mma(af[kk & 1], bfr[kk & 1]);
+      sched_from<0, NM, NR, 0>();
     }
-    // Instruction order for the slab (scheduling groups): the first step's
-    // fragment reads, then each later step's reads spread evenly over the
-    // matrix instructions of the step before it.  A K-contiguous fragment is
-    // one LDS read, a transposed one two.
-    {
-      constexpr int NR = (AK ? TM : 2 * TM) + (BKC ? TN : 2 * TN);
-      constexpr int NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
-      constexpr int RPG = NR / NM > 0 ? NR / NM : 1;   // reads per group
-      constexpr int NG = NR / RPG;
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-      for (int kk = 0; kk + 1 < KB / 16; ++kk) {
-#pragma unroll
-        for (int r = 0; r < NG; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, RPG, 0);
-        }
-        if (NM - PER * NG > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NG, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-    }
-
-    cur = (cur + 1 == NS) ? 0 : cur + 1;
-    nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
+    mma(af[(KS - 1) & 1], bfr[(KS - 1) & 1]);
   }
+  // The last requests (repeats of the final slab into idle stages) must
+  // land before the workgroup's LDS is released.
+  wait_vmcnt<0>();
 
   // ---- epilogue: lane holds C[m][n..n+3] for each (i, j, q) ----
   const Epilogue& e = g.epi;
@@ -490,12 +541,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int KB, int NS, bool AK, bool BKC>
+template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  dim3 grid(ntm * ntn), block(256);
+  dim3 grid(ntm * ntn), block(64 * NW);
 #define Q3L_GK(E) \
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, KB, NS, AK, BKC, E>), grid, block, 0, s, g)
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, KB, NS, NW, AK, BKC, E>), grid, block, 0, s, g)
   switch (g.epi.kind) {
     case EPI_STORE: Q3L_GK(EPI_STORE); break;
     case EPI_PARTIAL: Q3L_GK(EPI_PARTIAL); break;
@@ -508,13 +559,13 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int KB, int NS>
+template <int BM, int BN, int KB, int NS, int NW>
 hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
   const bool ak = g.a.k_contig, bk = g.b.k_contig;
-  if (ak && bk) return launch_epi<BM, BN, KB, NS, true, true>(g, s);
-  if (ak && !bk) return launch_epi<BM, BN, KB, NS, true, false>(g, s);
-  if (!ak && !bk) return launch_epi<BM, BN, KB, NS, false, false>(g, s);
-  return launch_epi<BM, BN, KB, NS, false, true>(g, s);
+  if (ak && bk) return launch_epi<BM, BN, KB, NS, NW, true, true>(g, s);
+  if (ak && !bk) return launch_epi<BM, BN, KB, NS, NW, true, false>(g, s);
+  if (!ak && !bk) return launch_epi<BM, BN, KB, NS, NW, false, false>(g, s);
+  return launch_epi<BM, BN, KB, NS, NW, false, true>(g, s);
 }
 
 }  // namespace
@@ -526,9 +577,9 @@ hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   auto tiles = [&](int bm, int bn) {
     return (int64_t)((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= kCUs) return launch_layout<256, 256, 64, 2>(g, s);
-  if (tiles(256, 128) >= kCUs) return launch_layout<256, 128, 64, 2>(g, s);
-  return launch_layout<128, 128, 64, 2>(g, s);
+  if (tiles(256, 256) >= kCUs) return launch_layout<256, 256, 64, 2, 8>(g, s);
+  if (tiles(256, 128) >= kCUs) return launch_layout<256, 128, 64, 2, 4>(g, s);
+  return launch_layout<128, 128, 64, 2, 4>(g, s);
 }
 
 }  // namespace q3l
