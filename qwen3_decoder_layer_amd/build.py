@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "libq3layer.so")
 SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "norm.hip",
            "attn_bf16.hip", "attn_f32.hip", "transpose.hip"]
 ARCH = "gfx950"
+# Per-source flags.  The attention kernels run softmax arithmetic on their
+# matrix-instruction results: keeping those accumulators in ordinary VGPRs
+# (not AGPRs) avoids a copy per value.
+EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -41,7 +45,8 @@ def compile_flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

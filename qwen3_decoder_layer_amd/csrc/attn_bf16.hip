@@ -21,6 +21,8 @@
 //     registers, so the G-head sum (adjoint of repeat_interleave) needs no
 //     atomics;
 //   dQ kernel: the forward's shape, accumulating dQ^T over key tiles.
+#include <type_traits>
+
 #include "common.h"
 #include "ops.h"
 
@@ -63,6 +65,10 @@ __device__ inline u32x4_t pack_half(const f32x16_t& s, int half) {
   return u32x4_t{pack2(s[b + 0], s[b + 1]), pack2(s[b + 2], s[b + 3]),
                  pack2(s[b + 4], s[b + 5]), pack2(s[b + 6], s[b + 7])};
 }
+
+// 2^x with the bare v_exp_f32: results below 2^-126 (probabilities that
+// small) flush to zero instead of taking the library's denormal-scaling path.
+__device__ inline float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================ forward =======================================
 template <int DH>
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
       // the result is exact, and the 64-multiply rescale is usually skipped.
       if (__any(mx > m_run + kTau)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_raw(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
 #pragma unroll
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pv = exp2f(fmaf(s[c][e], p.scale_log2, neg));
+          const float pv = exp2_raw(fmaf(s[c][e], p.scale_log2, neg));
           s[c][e] = pv;
           rs += pv;
         }
@@ -262,115 +268,147 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p, float* de
   }
 }
 
-// dK, dV for 128 keys of one kv head.
+// LDS row layout shared by the backward kernels: a [rows][d_h] bf16 tile
+// stored row-major with its 16-byte chunks permuted per row: chunk c of row
+// r sits at slot c ^ swz(r).  swz is a bijection on the low bits of r, so
+// the 16-byte reads of 16 consecutive rows at one chunk hit distinct banks,
+// and it moves the chunk PAIR {2m, 2m+1} as a unit with distinct pairs for
+// any 4 aligned consecutive rows, so the transposing 8-byte reads (4 rows x
+// 32 contiguous bytes per 16-lane group) are conflict-free as well.
+template <int CPR>
+__device__ inline int swz(int r) {
+  return ((r & (CPR / 2 - 1)) << 1) | ((r / (CPR / 2)) & 1);
+}
+
+// dK, dV for 128 keys of one kv head (32 per wave).  K and V of those keys
+// and double-buffered Q / dO tiles of QT queries sit in LDS in the layout
+// above, filled by direct global->LDS loads (no registers, no LDS store
+// instructions); the transposed operands of dV^T += dO^T P^T and
+// dK^T += Q^T dS^T come from transposing LDS reads of the same tiles.
 template <int DH>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
-  constexpr int DHP = DH + 8;
   constexpr int NKK = DH / 16, NDT = DH / 32;
-  constexpr int QT = 64;   // queries per tile
-  // Per stage: Q [QT][DHP], Q^T [DH][QT+8], dO [QT][DHP], dO^T [DH][QT+8].
-  constexpr int STAGE = 2 * QT * DHP + 2 * DH * (QT + 8);
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][STAGE];
-  __shared__ __attribute__((aligned(16))) float sL[2][QT];
-  __shared__ __attribute__((aligned(16))) float sD[2][QT];
+  constexpr int QT = 64, KB = 128;             // queries per tile, keys per workgroup
+  constexpr int RB = 2 * DH;                   // bytes per row
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;               // rows per direct-load instruction
+  constexpr int KVB = KB * RB, TB = QT * RB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KVB + 4 * TB];
+  __shared__ __attribute__((aligned(16))) float sLD[2][2][QT];   // [stage][lse, delta][q]
+  Q3L_LDS char* lds = (Q3L_LDS char*)smem;
+  Q3L_LDS char* sK = lds;
+  Q3L_LDS char* sV = lds + KVB;
+  Q3L_LDS float* ldsLD = (Q3L_LDS float*)&sLD[0][0][0];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
   const int l32 = lane & 31, h = lane >> 5;
   const int b = blockIdx.x / p.h_kv, kvh = blockIdx.x % p.h_kv;
-  const int kb0 = blockIdx.y * 128;       // first key of the workgroup
+  const int kb0 = blockIdx.y * KB;
   const int kw0 = kb0 + 32 * wave;        // first key of this wave
   const int L = p.L;
   const int64_t tok0 = (int64_t)b * L;
   const int mykv = kw0 + l32;
 
-  // K and V fragments of this wave's 32 keys (second MFMA operand).
-  u32x4_t kf[NKK], vf[NKK];
-  {
-    const int kr = min(mykv, L - 1);
-    const bf16_t* kp = p.k + (tok0 + kr) * p.ldk + (int64_t)kvh * DH + 8 * h;
-    const bf16_t* vp = p.v + (tok0 + kr) * p.ldv + (int64_t)kvh * DH + 8 * h;
+  // Rows r0 .. r0+NR-1 (token positions of sequence b, zero past L) of
+  // columns col0 .. col0+DH-1 of a [T][ld] matrix into an LDS tile.
+  auto load_rows = [&](auto nr, const bf16_t* base, int64_t ld, int col0, int r0,
+                       Q3L_LDS char* dst) {
+    constexpr int NR = decltype(nr)::value;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kf[kk] = ld16(kp + 16 * kk);
-      vf[kk] = ld16(vp + 16 * kk);
+    for (int j = 0; j < NR / RPI / 4; ++j) {
+      const int i = wave + 4 * j;
+      const int row = RPI * i + lane / CPR;
+      const int c = (lane % CPR) ^ swz<CPR>(row);
+      const int gr = r0 + row;
+      const uint32_t off =
+          gr < L ? (uint32_t)(((tok0 + gr) * ld + col0 + 8 * c) * 2) : kOOB;
+      lds_dma16((uint64_t)base, off, 0u, uni(lds_addr(dst + 1024 * i)));
     }
-  }
-  f32x16_t dkt[NDT], dvt[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { dkt[dt][e] = 0.f; dvt[dt][e] = 0.f; }
+  };
+  using KBc = std::integral_constant<int, KB>;
+  using QTc = std::integral_constant<int, QT>;
 
   // Query tiles: for each q head of the group, tiles from the one holding
   // key kb0 to the end of the sequence.
   const int qt_first = kb0 / QT;
   const int nqt = (L + QT - 1) / QT - qt_first;
   const int total = nqt * p.G;
-
-  // Loader: threads 0..127 own one 8x8 block of Q, 128..255 one of dO.
-  const int sel = tid >> 7, bt = tid & 127;
-  const int qb = bt % (QT / 8), db = bt / (QT / 8);
-  const bool lact = db < DH / 8;
-  u32x4_t reg[8];
-  float lreg = 0.f;
-  auto load_tile = [&](int it) {
+  auto stage = [&](int s) { return lds + 2 * KVB + s * 2 * TB; };   // Q, then dO
+  auto load_tile = [&](int it, int s) {
     const int head = kvh * p.G + it / nqt;
     const int q0 = (qt_first + it % nqt) * QT;
-    if (lact) {
-      const bf16_t* base = sel ? p.dout : p.q;
-      const int64_t ld = sel ? p.lddo : p.ldq;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int q = q0 + 8 * qb + r;
-        reg[r] = q < L ? ld16(base + (tok0 + q) * ld + (int64_t)head * DH + 8 * db) : zero4();
-      }
+    load_rows(QTc{}, p.q, p.ldq, head * DH, q0, stage(s));
+    load_rows(QTc{}, p.dout, p.lddo, head * DH, q0, stage(s) + TB);
+    if (wave < 2) {   // log-sum-exp (wave 0) and row sums (wave 1), 64 floats each
+      const float* src = wave == 0 ? (const float*)p.lse : p.delta;
+      const int q = q0 + lane;
+      const uint32_t off =
+          q < L ? (uint32_t)((((int64_t)b * p.h_q + head) * L + q) * 4) : kOOB;
+      lds_dma4((uint64_t)src, off, uni(lds_addr(ldsLD + (2 * s + wave) * QT)));
     }
-    if (tid < 2 * QT) {
-      const int q = q0 + (tid % QT);
-      const int64_t idx = ((int64_t)b * p.h_q + head) * L + min(q, L - 1);
-      lreg = tid < QT ? p.lse[idx] * kLog2e : p.delta[idx];
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16_t* S = smem[buf];
-    bf16_t* nat = S + sel * (QT * DHP + DH * (QT + 8));
-    bf16_t* tr = nat + QT * DHP;
-    if (lact) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) st16(nat + (8 * qb + r) * DHP + 8 * db, reg[r]);
-      u32x4_t t8[8];
-      transpose8x8(reg, t8);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) st16(tr + (8 * db + c) * (QT + 8) + 8 * qb, t8[c]);
-    }
-    if (tid < QT) sL[buf][tid] = lreg;
-    else if (tid < 2 * QT) sD[buf][tid - QT] = lreg;
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  load_rows(KBc{}, p.k, p.ldk, kvh * DH, kb0, sK);
+  load_rows(KBc{}, p.v, p.ldv, kvh * DH, kb0, sV);
+  load_tile(0, 0);
+  wait_vmcnt<0>();
+  stage_barrier();
+
+  // Per-lane LDS offsets.  16-byte reads (rows 32c + l32 of a Q/dO tile and
+  // rows 32 wave + l32 of K/V all share swz(l32)): chunk 2kk + h.
+  uint32_t offq[NKK];
+  {
+    const int sw = swz<CPR>(l32);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) offq[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
+  }
+  const uint32_t rowq = (uint32_t)l32 * RB, rowk = (uint32_t)(32 * wave + l32) * RB;
+  // Transposing reads for the dO^T / Q^T operands: 16-lane group g, source
+  // lane sl points at row 16 ks + 4 (g / 2) + sl / 4 (+8 for the second
+  // read), columns 32 dt + 16 (g % 2) + 4 (sl % 4) .. +3.
+  uint32_t offt[2][NDT];
+  uint32_t rowt;
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    const int tq = 4 * (g >> 1) + (sl >> 2);
+    const int tc = 2 * (g & 1) + ((sl & 3) >> 1);
+    rowt = (uint32_t)tq * RB + 8u * (sl & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      offt[0][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq)) << 4);
+      offt[1][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq + 8)) << 4) + 8u * RB;
+    }
+  }
+
+  f32x16_t dkt[NDT], dvt[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dkt[dt][e] = 0.f; dvt[dt][e] = 0.f; }
+
   for (int it = 0; it < total; ++it) {
-    const bool more = it + 1 < total;
-    if (more) load_tile(it + 1);
+    const int s = it & 1;
+    if (it + 1 < total) load_tile(it + 1, s ^ 1);
     const int q0 = (qt_first + it % nqt) * QT;
-    const int buf = it & 1;
     // Skip tiles entirely before this wave's keys (all masked).
     if (q0 + QT - 1 >= kw0 && kw0 < L) {
-      const bf16_t* sQ = smem[buf];
-      const bf16_t* sQt = sQ + QT * DHP;
-      const bf16_t* sO = sQt + DH * (QT + 8);
-      const bf16_t* sOt = sO + QT * DHP;
-      f32x16_t s[2], dp[2];
+      const Q3L_LDS char* sQ = stage(s);
+      const Q3L_LDS char* sO = sQ + TB;
+      f32x16_t sc[2], dp[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { s[c][e] = 0.f; dp[c][e] = 0.f; }
+        for (int e = 0; e < 16; ++e) { sc[c][e] = 0.f; dp[c][e] = 0.f; }
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int off = (32 * c + l32) * DHP + 16 * kk + 8 * h;
-          s[c] = mfma32(ld16(sQ + off), kf[kk], s[c]);
-          dp[c] = mfma32(ld16(sO + off), vf[kk], dp[c]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4_t ka = ld_lds16(sK + rowk + offq[kk]);
+        const u32x4_t va = ld_lds16(sV + rowk + offq[kk]);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t o = rowq + 32u * RB * c + offq[kk];
+          sc[c] = mfma32(ld_lds16(sQ + o), ka, sc[c]);
+          dp[c] = mfma32(ld_lds16(sO + o), va, dp[c]);
         }
       }
       // lane: key mykv; rows q = q0 + 32c + 8(e/4) + 4h + e%4 -- four
@@ -381,34 +419,36 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int qb = 32 * c + 8 * e4 + 4 * h;
-          const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sL[buf][qb]);
-          const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][qb]);
+          const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qb]) * kLog2e;
+          const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qb]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * e4 + r;
-            float pv = exp2f(fmaf(s[c][e], p.scale_log2, -lq[r]));
+            float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, -lq[r]));
             if (need_mask) {
               const int q = q0 + qb + r;
               if (mykv > q || q >= L || mykv >= L) pv = 0.f;
             }
-            s[c][e] = pv;
+            sc[c][e] = pv;
             dp[c][e] = pv * (dp[c][e] - dq4[r]);
           }
         }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pf = pack_half(s[ks >> 1], ks & 1);
+        const u32x4_t pf = pack_half(sc[ks >> 1], ks & 1);
         const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);
+        const uint32_t rk = rowt + 16u * RB * ks;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const int off = (32 * dt + l32) * (QT + 8) + 16 * ks + 4 * h;
-          dvt[dt] = mfma32(ld_pair8(sOt + off), pf, dvt[dt]);
-          dkt[dt] = mfma32(ld_pair8(sQt + off), df, dkt[dt]);
+          const u32x2_t o0 = ld_tr8(sO + rk + offt[0][dt]), o1 = ld_tr8(sO + rk + offt[1][dt]);
+          const u32x2_t q0v = ld_tr8(sQ + rk + offt[0][dt]), q1v = ld_tr8(sQ + rk + offt[1][dt]);
+          dvt[dt] = mfma32(u32x4_t{o0[0], o0[1], o1[0], o1[1]}, pf, dvt[dt]);
+          dkt[dt] = mfma32(u32x4_t{q0v[0], q0v[1], q1v[0], q1v[1]}, df, dkt[dt]);
         }
       }
     }
-    if (more) store_tile((it + 1) & 1);
-    __syncthreads();
+    wait_vmcnt<0>();      // this wave's part of tile it+1 has landed
+    stage_barrier();      // everyone's part; stage s fully read
   }
 
   if (mykv >= L) return;
@@ -547,7 +587,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float pv = exp2f(fmaf(s[c][e], p.scale_log2, -lse2));
+          float pv = exp2_raw(fmaf(s[c][e], p.scale_log2, -lse2));
           if (need_mask) {
             const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
             if (kv > qrow || kv >= L) pv = 0.f;

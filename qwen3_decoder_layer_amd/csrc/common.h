@@ -100,4 +100,67 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
   return (a + b - 1) / b;
 }
 
+// ---- LDS: direct loads from global memory and transposing reads ----------
+#define Q3L_LDS __attribute__((address_space(3)))
+
+__device__ inline uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint64_t uni64(uint64_t v) {
+  return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v);
+}
+__device__ inline uint32_t lds_addr(const Q3L_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+constexpr uint32_t kOOB = 0x80000000u;   // any offset past the buffer range
+
+// Global -> LDS without registers: lane i's 16 (lds_dma16) or 4 (lds_dma4)
+// bytes land at LDS byte lds_base + 16 i (4 i); lds_base is uniform.  The
+// buffer covers [p, p + 2 GiB) with stride 0, so `voff + soff` (per-lane +
+// uniform) is a byte offset and an offset >= 2^31 (kOOB) reads zeros.  These
+// writes are counted by vmcnt; a kernel orders them against its own LDS
+// reads with an explicit s_waitcnt vmcnt and a barrier.
+__device__ inline void lds_dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ inline void lds_dma4(uint64_t p, uint32_t voff, uint32_t lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 4,
+                                           voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for LDS stages: this wave's LDS reads have returned (so
+// a stage it read may be refilled once everyone is past), without the
+// vmcnt(0) a fenced __syncthreads() would add -- direct loads of younger
+// stages stay in flight.  The memory clobber keeps LDS accesses on their
+// side of it.
+__device__ inline void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ inline u32x4_t ld_lds16(const Q3L_LDS void* p) {
+  return *reinterpret_cast<const Q3L_LDS u32x4_t*>(p);
+}
+// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16).  In
+// each 16-lane group, output lane j receives element (j % 4) of the 8 bytes
+// addressed by source lanes 4e + j / 4, e = 0..3, as its element e.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ inline u32x2_t ld_tr8(const Q3L_LDS void* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((Q3L_LDS i16x4_t*)(p)));
+}
+// Two transposing reads (at p and p + second bytes) forming one MFMA operand.
+__device__ inline u32x4_t ld_tr_pair(const Q3L_LDS void* p, int second) {
+  const u32x2_t a = ld_tr8(p);
+  const u32x2_t b = ld_tr8((const Q3L_LDS char*)p + second);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
 }  // namespace q3l

@@ -42,30 +42,6 @@
 namespace q3l {
 namespace {
 
-constexpr uint32_t kOOB = 0x80000000u;   // any offset past the buffer range
-
-#define Q3L_LDS __attribute__((address_space(3)))
-
-__device__ inline uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ inline uint64_t uni64(uint64_t v) {
-  return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v);
-}
-
-// 16 bytes per lane from a raw buffer straight into LDS: lane i's data lands
-// at LDS byte lds_base + 16 * i.  The buffer covers [p, p + 2 GiB) with
-// stride 0, so `voff + soff` (per-lane + uniform) is a byte offset and any
-// offset >= 2^31 reads zeros.  The kernel orders these writes against its
-// LDS reads itself: an explicit s_waitcnt vmcnt before each stage barrier.
-__device__ inline void dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16,
-                                           voff, soff, 0, 0);
-}
-__device__ inline uint32_t lds_addr(const Q3L_LDS char* p) {
-  return (uint32_t)(uintptr_t)p;
-}
-
 // Segment holding index idx of an operand (idx uniform): base pointer, ld
 // (elements) and start.  Every field is read from the kernel argument through
 // readfirstlane before the select, so the compiler keeps the choice between
@@ -145,7 +121,7 @@ struct KOperand {
   // the scalar offset.
   __device__ void issue_one(const Operand&, int i, int k0, int, bool last,
                             Q3L_LDS char* dst, int wave) const {
-    dma16(base[i], last ? vtail[i] : voff[i], uni(2u * (uint32_t)k0),
+    lds_dma16(base[i], last ? vtail[i] : voff[i], uni(2u * (uint32_t)k0),
           uni(lds_addr(dst + 1024 * (NW * i + wave))));
   }
 };
@@ -191,21 +167,10 @@ struct ROperand {
     const int k = k0 + krl[i];
     const uint32_t off =
         k < K ? (uint32_t)(((int64_t)(k - st) * ld + col[i]) * 2) : kOOB;
-    dma16(p, off, 0u, uni(lds_addr(dst + 1024 * (NW * i + wave))));
+    lds_dma16(p, off, 0u, uni(lds_addr(dst + 1024 * (NW * i + wave))));
   }
 };
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-__device__ inline u32x4_t ld_tr2(const Q3L_LDS char* p, int second) {
-  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Q3L_LDS i16x4_t*)(p));
-  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((Q3L_LDS i16x4_t*)(p + second));
-  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
-  return u32x4_t{ua[0], ua[1], ub[0], ub[1]};
-}
-
-__device__ inline u32x4_t ld_lds16(const Q3L_LDS char* p) {
-  return *reinterpret_cast<const Q3L_LDS u32x4_t*>(p);
-}
 
 // ---- tile order -----------------------------------------------------------
 __device__ inline void map_tile(int bid, int nb, int ntm, int ntn, int& tm,
@@ -264,7 +229,7 @@ struct RFrag {
     }
   }
   __device__ u32x4_t read(const Q3L_LDS char* t, int kk, int i) const {
-    return ld_tr2(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
+    return ld_tr_pair(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
   }
 };
 
@@ -278,17 +243,6 @@ template <int ROWS, int TT, int KB, int NW> struct OpSel<ROWS, TT, KB, NW, false
   RFrag<TT, ROWS> fr;
 };
 
-template <int N>
-__device__ inline void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Workgroup barrier for the LDS stages: this wave's LDS reads have returned
-// (so a stage it read may be refilled once everyone is past), without the
-// vmcnt(0) a fenced __syncthreads() would add -- younger slabs' requests
-// stay in flight.  The memory clobber keeps LDS accesses on their side.
-__device__ inline void stage_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Scheduling groups for one k-step of NM matrix instructions: the NR LDS
 // fragment reads of the next step go out early (one after each of the first
