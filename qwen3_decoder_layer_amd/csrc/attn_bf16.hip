@@ -280,6 +280,56 @@ __device__ inline int swz(int r) {
   return ((r & (CPR / 2 - 1)) << 1) | ((r / (CPR / 2)) & 1);
 }
 
+// Rows r0 .. r0+NR-1 (token positions of one sequence starting at token
+// tok0, zero past L) of columns col0 .. col0+DH-1 of a [T][ld] bf16 matrix
+// into an LDS tile in the layout above, by direct loads shared among the NW
+// waves of the workgroup (1 KB per wave-instruction).
+template <int DH, int NR, int NW>
+__device__ inline void load_rows_lds(const bf16_t* base, int64_t ld, int64_t tok0, int col0,
+                                     int r0, int L, Q3L_LDS char* dst, int wave, int lane) {
+  constexpr int RB = 2 * DH, CPR = RB / 16, RPI = 1024 / RB;
+  static_assert(NR % (RPI * NW) == 0, "whole instructions per wave");
+#pragma unroll
+  for (int j = 0; j < NR / RPI / NW; ++j) {
+    const int i = wave + NW * j;
+    const int row = RPI * i + lane / CPR;
+    const int c = (lane % CPR) ^ swz<CPR>(row);
+    const int gr = r0 + row;
+    const uint32_t off = gr < L ? (uint32_t)(((tok0 + gr) * ld + col0 + 8 * c) * 2) : kOOB;
+    lds_dma16((uint64_t)base, off, 0u, uni(lds_addr(dst + 1024 * i)));
+  }
+}
+
+// Per-lane LDS byte offsets of the transposing reads that build a
+// [32 d][16 k] MFMA operand from a tile stored [k rows][d]: 16-lane group g,
+// source lane sl points at row 4 (g / 2) + sl / 4 (+8 for the second read)
+// of a 16-row block, columns 32 dt + 16 (g % 2) + 4 (sl % 4) .. +3.
+// Output: row part `rowt` (add 16 RB per 16-row block) and per-dt column
+// parts for the two reads (the second includes its +8 rows).
+template <int DH>
+struct TrOffsets {
+  static constexpr int RB = 2 * DH, CPR = RB / 16, NDT = DH / 32;
+  uint32_t rowt;
+  uint32_t col[2][NDT];
+  __device__ void init(int lane) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int tq = 4 * (g >> 1) + (sl >> 2);
+    const int tc = 2 * (g & 1) + ((sl & 3) >> 1);
+    rowt = (uint32_t)tq * RB + 8u * (sl & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      col[0][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq)) << 4);
+      col[1][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq + 8)) << 4) + 8u * RB;
+    }
+  }
+  // Operand for 16-row block `blk`, 32-column block dt of tile t.
+  __device__ u32x4_t read(const Q3L_LDS char* t, int blk, int dt) const {
+    const Q3L_LDS char* r = t + rowt + 16u * RB * blk;
+    const u32x2_t a = ld_tr8(r + col[0][dt]), b = ld_tr8(r + col[1][dt]);
+    return u32x4_t{a[0], a[1], b[0], b[1]};
+  }
+};
+
 // dK, dV for 128 keys of one kv head (32 per wave).  K and V of those keys
 // and double-buffered Q / dO tiles of QT queries sit in LDS in the layout
 // above, filled by direct global->LDS loads (no registers, no LDS store
@@ -310,25 +360,6 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
   const int64_t tok0 = (int64_t)b * L;
   const int mykv = kw0 + l32;
 
-  // Rows r0 .. r0+NR-1 (token positions of sequence b, zero past L) of
-  // columns col0 .. col0+DH-1 of a [T][ld] matrix into an LDS tile.
-  auto load_rows = [&](auto nr, const bf16_t* base, int64_t ld, int col0, int r0,
-                       Q3L_LDS char* dst) {
-    constexpr int NR = decltype(nr)::value;
-#pragma unroll
-    for (int j = 0; j < NR / RPI / 4; ++j) {
-      const int i = wave + 4 * j;
-      const int row = RPI * i + lane / CPR;
-      const int c = (lane % CPR) ^ swz<CPR>(row);
-      const int gr = r0 + row;
-      const uint32_t off =
-          gr < L ? (uint32_t)(((tok0 + gr) * ld + col0 + 8 * c) * 2) : kOOB;
-      lds_dma16((uint64_t)base, off, 0u, uni(lds_addr(dst + 1024 * i)));
-    }
-  };
-  using KBc = std::integral_constant<int, KB>;
-  using QTc = std::integral_constant<int, QT>;
-
   // Query tiles: for each q head of the group, tiles from the one holding
   // key kb0 to the end of the sequence.
   const int qt_first = kb0 / QT;
@@ -338,8 +369,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
   auto load_tile = [&](int it, int s) {
     const int head = kvh * p.G + it / nqt;
     const int q0 = (qt_first + it % nqt) * QT;
-    load_rows(QTc{}, p.q, p.ldq, head * DH, q0, stage(s));
-    load_rows(QTc{}, p.dout, p.lddo, head * DH, q0, stage(s) + TB);
+    load_rows_lds<DH, QT, 4>(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave, lane);
+    load_rows_lds<DH, QT, 4>(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave, lane);
     if (wave < 2) {   // log-sum-exp (wave 0) and row sums (wave 1), 64 floats each
       const float* src = wave == 0 ? (const float*)p.lse : p.delta;
       const int q = q0 + lane;
@@ -349,8 +380,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
     }
   };
 
-  load_rows(KBc{}, p.k, p.ldk, kvh * DH, kb0, sK);
-  load_rows(KBc{}, p.v, p.ldv, kvh * DH, kb0, sV);
+  load_rows_lds<DH, KB, 4>(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave, lane);
+  load_rows_lds<DH, KB, 4>(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave, lane);
   load_tile(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
@@ -364,22 +395,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
     for (int kk = 0; kk < NKK; ++kk) offq[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
   }
   const uint32_t rowq = (uint32_t)l32 * RB, rowk = (uint32_t)(32 * wave + l32) * RB;
-  // Transposing reads for the dO^T / Q^T operands: 16-lane group g, source
-  // lane sl points at row 16 ks + 4 (g / 2) + sl / 4 (+8 for the second
-  // read), columns 32 dt + 16 (g % 2) + 4 (sl % 4) .. +3.
-  uint32_t offt[2][NDT];
-  uint32_t rowt;
-  {
-    const int g = lane >> 4, sl = lane & 15;
-    const int tq = 4 * (g >> 1) + (sl >> 2);
-    const int tc = 2 * (g & 1) + ((sl & 3) >> 1);
-    rowt = (uint32_t)tq * RB + 8u * (sl & 1);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      offt[0][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq)) << 4);
-      offt[1][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq + 8)) << 4) + 8u * RB;
-    }
-  }
+  // Transposing reads for the dO^T / Q^T operands.
+  TrOffsets<DH> tro;
+  tro.init(lane);
 
   f32x16_t dkt[NDT], dvt[NDT];
 #pragma unroll
@@ -437,13 +455,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4_t pf = pack_half(sc[ks >> 1], ks & 1);
         const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);
-        const uint32_t rk = rowt + 16u * RB * ks;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const u32x2_t o0 = ld_tr8(sO + rk + offt[0][dt]), o1 = ld_tr8(sO + rk + offt[1][dt]);
-          const u32x2_t q0v = ld_tr8(sQ + rk + offt[0][dt]), q1v = ld_tr8(sQ + rk + offt[1][dt]);
-          dvt[dt] = mfma32(u32x4_t{o0[0], o0[1], o1[0], o1[1]}, pf, dvt[dt]);
-          dkt[dt] = mfma32(u32x4_t{q0v[0], q0v[1], q1v[0], q1v[1]}, df, dkt[dt]);
+          dvt[dt] = mfma32(tro.read(sO, ks, dt), pf, dvt[dt]);
+          dkt[dt] = mfma32(tro.read(sQ, ks, dt), df, dkt[dt]);
         }
       }
     }
@@ -468,14 +483,19 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
 }
 
 // dQ for 32 query rows per wave (grid and wave roles as in the forward).
+// K/V tiles of KT keys are double-buffered in LDS in the swizzled row layout
+// by direct loads; the K^T operand of dQ^T += K^T dS^T comes from
+// transposing reads of the same K tile.
 template <int DH>
 __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
-  constexpr int DHP = DH + 8;
   constexpr int NKK = DH / 16, NDT = DH / 32;
-  constexpr int STAGE = 2 * KT * DHP + DH * KTP;   // K, V, K^T
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][STAGE];
+  constexpr int RB = 2 * DH, CPR = RB / 16;
+  constexpr int TB = KT * RB;                  // one K or V tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+  Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
   const int l32 = lane & 31, h = lane >> 5;
   const int ngroups = p.G / p.hb;
   const int b = blockIdx.x / (p.h_kv * ngroups);
@@ -495,6 +515,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   const int qrow = qw0 + l32;
   const int qr = min(qrow, L - 1);
 
+  // Q and dO fragments of this wave's rows (second MFMA operand).
   u32x4_t qf[NKK], of[NKK];
   {
     const bf16_t* qp = p.q + (tok0 + qr) * p.ldq + (int64_t)head * DH + 8 * h;
@@ -509,49 +530,21 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   const float lse2 = p.lse[sidx] * kLog2e;
   const float dlt = p.delta[sidx];
 
-  // Loader: K and V natural (16-byte chunks), K^T via 8x8 register blocks.
-  constexpr int KCH = KT * DH / 8 / 256;
-  u32x4_t kreg[KCH], vreg[KCH], treg[8];
-  const bool tact = tid < (KT / 8) * (DH / 8);
-  const int tkb = tid % (KT / 8), tdb = tid / (KT / 8);
-  auto load_tile = [&](int t) {
-    const int kv0 = t * KT;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (DH / 8), cc = c % (DH / 8);
-      const int kv = kv0 + row;
-      const bool ok = kv < L;
-      kreg[i] = ok ? ld16(p.k + (tok0 + kv) * p.ldk + (int64_t)kvh * DH + 8 * cc) : zero4();
-      vreg[i] = ok ? ld16(p.v + (tok0 + kv) * p.ldv + (int64_t)kvh * DH + 8 * cc) : zero4();
-    }
-    if (tact) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int kv = kv0 + 8 * tkb + r;
-        treg[r] = kv < L ? ld16(p.k + (tok0 + kv) * p.ldk + (int64_t)kvh * DH + 8 * tdb)
-                         : zero4();
-      }
-    }
+  auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
+  auto load_tile = [&](int t, int s) {
+    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave, lane);
+    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave, lane);
   };
-  auto store_tile = [&](int buf) {
-    bf16_t* sK = smem[buf];
-    bf16_t* sV = sK + KT * DHP;
-    bf16_t* sKt = sV + KT * DHP;
+  // 16-byte reads of rows 32c + l32 (chunk 2kk + h).
+  uint32_t offk[NKK];
+  {
+    const int sw = swz<CPR>(l32);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (DH / 8), cc = c % (DH / 8);
-      st16(sK + row * DHP + 8 * cc, kreg[i]);
-      st16(sV + row * DHP + 8 * cc, vreg[i]);
-    }
-    if (tact) {
-      u32x4_t t8[8];
-      transpose8x8(treg, t8);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) st16(sKt + (8 * tdb + c) * KTP + 8 * tkb, t8[c]);
-    }
-  };
+    for (int kk = 0; kk < NKK; ++kk) offk[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
+  }
+  const uint32_t rowk = (uint32_t)l32 * RB;
+  TrOffsets<DH> tro;
+  tro.init(lane);
 
   f32x16_t dqt[NDT];
 #pragma unroll
@@ -559,27 +552,26 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqt[dt][e] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  load_tile(0, 0);
+  wait_vmcnt<0>();
+  stage_barrier();
   for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
+    const int s = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, s ^ 1);
     if (t < my_tiles) {
-      const bf16_t* sK = smem[t & 1];
-      const bf16_t* sV = sK + KT * DHP;
-      const bf16_t* sKt = sV + KT * DHP;
+      const Q3L_LDS char* sK = stage(s);
+      const Q3L_LDS char* sV = sK + TB;
       const int kv0 = t * KT;
-      f32x16_t s[2], dp[2];
+      f32x16_t sc[2], dp[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { s[c][e] = 0.f; dp[c][e] = 0.f; }
+        for (int e = 0; e < 16; ++e) { sc[c][e] = 0.f; dp[c][e] = 0.f; }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const int off = (32 * c + l32) * DHP + 16 * kk + 8 * h;
-          s[c] = mfma32(ld16(sK + off), qf[kk], s[c]);
-          dp[c] = mfma32(ld16(sV + off), of[kk], dp[c]);
+          const uint32_t o = rowk + 32u * RB * c + offk[kk];
+          sc[c] = mfma32(ld_lds16(sK + o), qf[kk], sc[c]);
+          dp[c] = mfma32(ld_lds16(sV + o), of[kk], dp[c]);
         }
       }
       const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
@@ -587,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float pv = exp2_raw(fmaf(s[c][e], p.scale_log2, -lse2));
+          float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, -lse2));
           if (need_mask) {
             const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
             if (kv > qrow || kv >= L) pv = 0.f;
@@ -598,13 +590,11 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          dqt[dt] = mfma32(ld_pair8(sKt + (32 * dt + l32) * KTP + 16 * ks + 4 * h), df,
-                           dqt[dt]);
+        for (int dt = 0; dt < NDT; ++dt) dqt[dt] = mfma32(tro.read(sK, ks, dt), df, dqt[dt]);
       }
     }
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
+    wait_vmcnt<0>();
+    stage_barrier();
   }
 
   if (qrow >= L) return;
