@@ -6,20 +6,23 @@
 //   each wave owns 32 query rows of one q head; the workgroup covers the
 //   G' = min(G, 4) q heads of a kv group (times 4/G' row blocks), so every
 //   K/V tile staged in LDS serves 128 (row, head) pairs.  K/V tiles of 64
-//   keys are double-buffered in LDS (V transposed in registers on the way
-//   in).  Scores are computed transposed, S^T = K Q^T, so that each lane owns
-//   one query: the online-softmax statistics (running max m, running sum l,
-//   the merge rule of the state-placement page's ring-attention section) are
-//   per lane, and the probabilities feed O^T = V^T P^T straight from the
+//   keys are double-buffered in LDS, filled by direct global->LDS loads in
+//   their natural [key][d] layout (16-byte chunks permuted per row against
+//   bank conflicts); V^T operands come from transposing LDS reads.  Scores
+//   are computed transposed, S^T = K Q^T, so that each lane owns one query:
+//   the online-softmax statistics (running max m, running sum l, the merge
+//   rule of the state-placement page's ring-attention section) are per
+//   lane, and the probabilities feed O^T = V^T P^T straight from the
 //   accumulators.  Output: O (bf16) and the log-sum-exp per query (fp32).
 //
 // Backward (P recomputed from the saved log-sum-exp):
 //   delta = rowsum(dO * O) per query;
-//   dK/dV kernel: a workgroup owns 128 keys of one kv head (32 per wave,
-//     K and V fragments in registers) and sweeps every q head of the group
-//     and every query tile at or after its keys; dK^T and dV^T accumulate in
-//     registers, so the G-head sum (adjoint of repeat_interleave) needs no
-//     atomics;
+//   dK/dV kernel: a workgroup owns 128 keys of one kv head (32 per wave; K
+//     and V in LDS) and sweeps every q head of the group and every query
+//     tile at or after its keys (Q / dO tiles and their LSE / delta by
+//     direct loads, transposed operands by transposing reads); dK^T and
+//     dV^T accumulate in registers, so the G-head sum (adjoint of
+//     repeat_interleave) needs no atomics;
 //   dQ kernel: the forward's shape, accumulating dQ^T over key tiles.
 #include <type_traits>
 
@@ -33,7 +36,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int KT = 64;        // keys per tile
 constexpr float kTau = 8.0f;  // rescale threshold (log2 units), see the forward
-constexpr int KTP = KT + 8;   // padded row length of a transposed tile
 
 struct FwdP {
   int B, L, h_q, h_kv, G, hb, rb;
@@ -51,14 +53,6 @@ struct FwdP {
 
 __device__ inline u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
-// Two 8-byte LDS reads forming one MFMA k-operand whose 16 k-values, for lane
-// group h = lane / 32, are {4h..4h+3} and {8+4h..8+4h+3} of a 16-block (the
-// order in which a 32x32 accumulator holds rows).
-__device__ inline u32x4_t ld_pair8(const bf16_t* p) {
-  const u32x2_t a = ld8(p), b = ld8(p + 8);
-  return u32x4_t{a[0], a[1], b[0], b[1]};
-}
-
 // Pack accumulator values i = 8*half .. 8*half+7 (bf16) into a k-operand.
 __device__ inline u32x4_t pack_half(const f32x16_t& s, int half) {
   const int b = 8 * half;
@@ -70,205 +64,7 @@ __device__ inline u32x4_t pack_half(const f32x16_t& s, int half) {
 // small) flush to zero instead of taking the library's denormal-scaling path.
 __device__ inline float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ============================ forward =======================================
-template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
-  constexpr int DHP = DH + 8;
-  constexpr int NKK = DH / 16;   // k-steps over the head dim
-  constexpr int NDT = DH / 32;   // 32-row tiles of d
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * DHP];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * KTP];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int ngroups = p.G / p.hb;
-  const int b = blockIdx.x / (p.h_kv * ngroups);
-  const int rem = blockIdx.x % (p.h_kv * ngroups);
-  const int kvh = rem / ngroups, hg = rem % ngroups;
-  const int QB = 32 * p.rb;
-  const int qtile = gridDim.y - 1 - blockIdx.y;   // longest rows first
-  const int q0 = qtile * QB;
-  const int head = kvh * p.G + hg * p.hb + (wave % p.hb);
-  const int qw0 = q0 + 32 * (wave / p.hb);        // this wave's first row
-  const int L = p.L;
-  const int64_t tok0 = (int64_t)b * L;
-
-  // K/V tiles needed by the workgroup and by this wave.
-  const int qend = min(q0 + QB, L);
-  const int ntiles = (qend + KT - 1) / KT;
-  const int wave_last = min(qw0 + 31, L - 1);
-  const int my_tiles = qw0 < L ? wave_last / KT + 1 : 0;
-
-  // Q fragments (second MFMA operand: lane owns query row qw0 + l32).
-  u32x4_t qf[NKK];
-  {
-    const int qr = min(qw0 + l32, L - 1);
-    const bf16_t* qp = p.q + (tok0 + qr) * p.ldq + (int64_t)head * DH + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = ld16(qp + 16 * kk);
-  }
-
-  // ---- tile loaders ----
-  constexpr int KCH = KT * DH / 8 / 256;  // 16-byte K chunks per thread
-  u32x4_t kreg[KCH];
-  u32x4_t vreg[8];
-  // V^T blocks: key-block index fastest over lanes (conflict-free LDS stores).
-  const bool vact = tid < (KT / 8) * (DH / 8);
-  const int vkb = tid % (KT / 8), vdb = tid / (KT / 8);
-  auto load_tile = [&](int t) {
-    const int kv0 = t * KT;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (DH / 8), cc = c % (DH / 8);
-      const int kv = kv0 + row;
-      kreg[i] = kv < L ? ld16(p.k + (tok0 + kv) * p.ldk + (int64_t)kvh * DH + 8 * cc)
-                       : zero4();
-    }
-    if (vact) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int kv = kv0 + 8 * vkb + r;
-        vreg[r] = kv < L ? ld16(p.v + (tok0 + kv) * p.ldv + (int64_t)kvh * DH + 8 * vdb)
-                         : zero4();
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (DH / 8), cc = c % (DH / 8);
-      st16(&sK[buf][row * DHP + 8 * cc], kreg[i]);
-    }
-    if (vact) {
-      u32x4_t tr[8];
-      transpose8x8(vreg, tr);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) st16(&sVt[buf][(8 * vdb + c) * KTP + 8 * vkb], tr[c]);
-    }
-  };
-
-  f32x16_t oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int qrow = qw0 + l32;
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-    if (t < my_tiles) {
-      const bf16_t* Ks = sK[t & 1];
-      const bf16_t* Vt = sVt[t & 1];
-      const int kv0 = t * KT;
-      f32x16_t s[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[c][e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          s[c] = mfma32(ld16(Ks + (32 * c + l32) * DHP + 16 * kk + 8 * h), qf[kk], s[c]);
-      }
-      const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = s[c][e];
-          if (need_mask) {
-            const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (kv > qrow || kv >= L) v = -INFINITY;
-          }
-          s[c][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
-      // The reference maximum m_run moves (and O, l are rescaled) only when a
-      // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
-      // the result is exact, and the 64-multiply rescale is usually skipped.
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_raw(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-      }
-      const float neg = -m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = exp2_raw(fmaf(s[c][e], p.scale_log2, neg));
-          s[c][e] = pv;
-          rs += pv;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run += rs;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pf = pack_half(s[ks >> 1], ks & 1);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          oacc[dt] = mfma32(ld_pair8(Vt + (32 * dt + l32) * KTP + 16 * ks + 4 * h), pf,
-                            oacc[dt]);
-      }
-    }
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
-  }
-
-  if (qrow >= L) return;
-  const float inv = 1.0f / l_run;
-  bf16_t* op = p.o + (tok0 + qrow) * p.ldo + (int64_t)head * DH;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * dt + 8 * j + 4 * h;
-      st8(op + d, u32x2_t{pack2(oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv),
-                          pack2(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv)});
-    }
-  if (h == 0)
-    p.lse[((int64_t)b * p.h_q + head) * L + qrow] = (m_run + log2f(l_run)) * kLn2;
-}
-
-// ============================ backward ======================================
-// delta[b, h, t] = sum_d dO[t, h, d] * O[t, h, d]
-template <int DH>
-__global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p, float* delta) {
-  constexpr int LP = DH / 8;
-  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
-  const int j = threadIdx.x % LP;
-  const int64_t total = (int64_t)p.B * p.L * p.h_q;
-  const bool valid = item < total;
-  const int64_t it = valid ? item : 0;
-  const int64_t tok = it / p.h_q;
-  const int head = (int)(it % p.h_q);
-  const u32x4_t a = ld16(p.dout + tok * p.lddo + (int64_t)head * DH + 8 * j);
-  const u32x4_t o = ld16(p.o + tok * p.ldo + (int64_t)head * DH + 8 * j);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s += lo_f(a[e]) * lo_f(o[e]) + hi_f(a[e]) * hi_f(o[e]);
-  s = group_sum(s, LP);
-  if (valid && j == 0) {
-    const int64_t b = tok / p.L, t = tok % p.L;
-    delta[(b * p.h_q + head) * p.L + t] = s;
-  }
-}
-
-// LDS row layout shared by the backward kernels: a [rows][d_h] bf16 tile
+// LDS row layout of the K/V/Q/dO tiles: a [rows][d_h] bf16 tile
 // stored row-major with its 16-byte chunks permuted per row: chunk c of row
 // r sits at slot c ^ swz(r).  swz is a bijection on the low bits of r, so
 // the 16-byte reads of 16 consecutive rows at one chunk hit distinct banks,
@@ -329,6 +125,179 @@ struct TrOffsets {
     return u32x4_t{a[0], a[1], b[0], b[1]};
   }
 };
+
+// ============================ forward =======================================
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
+  constexpr int NKK = DH / 16;   // k-steps over the head dim
+  constexpr int NDT = DH / 32;   // 32-row tiles of d
+  constexpr int RB = 2 * DH, CPR = RB / 16;
+  constexpr int TB = KT * RB;    // one K or V tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // 2 stages of K, V
+  Q3L_LDS char* lds = (Q3L_LDS char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
+  const int l32 = lane & 31, h = lane >> 5;
+  const int ngroups = p.G / p.hb;
+  const int b = blockIdx.x / (p.h_kv * ngroups);
+  const int rem = blockIdx.x % (p.h_kv * ngroups);
+  const int kvh = rem / ngroups, hg = rem % ngroups;
+  const int QB = 32 * p.rb;
+  const int qtile = gridDim.y - 1 - blockIdx.y;   // longest rows first
+  const int q0 = qtile * QB;
+  const int head = kvh * p.G + hg * p.hb + (wave % p.hb);
+  const int qw0 = q0 + 32 * (wave / p.hb);        // this wave's first row
+  const int L = p.L;
+  const int64_t tok0 = (int64_t)b * L;
+
+  // K/V tiles needed by the workgroup and by this wave.
+  const int qend = min(q0 + QB, L);
+  const int ntiles = (qend + KT - 1) / KT;
+  const int wave_last = min(qw0 + 31, L - 1);
+  const int my_tiles = qw0 < L ? wave_last / KT + 1 : 0;
+
+  // Q fragments (second MFMA operand: lane owns query row qw0 + l32).
+  u32x4_t qf[NKK];
+  {
+    const int qr = min(qw0 + l32, L - 1);
+    const bf16_t* qp = p.q + (tok0 + qr) * p.ldq + (int64_t)head * DH + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = ld16(qp + 16 * kk);
+  }
+
+  // K and V tiles by direct loads; V^T operands by transposing reads.
+  auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
+  auto load_tile = [&](int t, int s) {
+    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave, lane);
+    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave, lane);
+  };
+  uint32_t offk[NKK];
+  {
+    const int sw = swz<CPR>(l32);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) offk[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
+  }
+  const uint32_t rowk = (uint32_t)l32 * RB;
+  TrOffsets<DH> tro;
+  tro.init(lane);
+
+  f32x16_t oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qrow = qw0 + l32;
+
+  load_tile(0, 0);
+  wait_vmcnt<0>();
+  stage_barrier();
+  for (int t = 0; t < ntiles; ++t) {
+    const int s = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, s ^ 1);
+    if (t < my_tiles) {
+      const Q3L_LDS char* sK = stage(s);
+      const Q3L_LDS char* sV = sK + TB;
+      const int kv0 = t * KT;
+      f32x16_t sc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[c][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          sc[c] = mfma32(ld_lds16(sK + rowk + 32u * RB * c + offk[kk]), qf[kk], sc[c]);
+      }
+      const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = sc[c][e];
+          if (need_mask) {
+            const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (kv > qrow || kv >= L) v = -INFINITY;
+          }
+          sc[c][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
+      // The reference maximum m_run moves (and O, l are rescaled) only when a
+      // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
+      // the result is exact, and the 64-multiply rescale is usually skipped.
+      if (__any(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_raw(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      }
+      const float neg = -m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, neg));
+          sc[c][e] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l_run += rs;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4_t pf = pack_half(sc[ks >> 1], ks & 1);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(tro.read(sV, ks, dt), pf, oacc[dt]);
+      }
+    }
+    wait_vmcnt<0>();
+    stage_barrier();
+  }
+
+  if (qrow >= L) return;
+  const float inv = 1.0f / l_run;
+  bf16_t* op = p.o + (tok0 + qrow) * p.ldo + (int64_t)head * DH;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * dt + 8 * j + 4 * h;
+      st8(op + d, u32x2_t{pack2(oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv),
+                          pack2(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv)});
+    }
+  if (h == 0)
+    p.lse[((int64_t)b * p.h_q + head) * L + qrow] = (m_run + log2f(l_run)) * kLn2;
+}
+
+// ============================ backward ======================================
+// delta[b, h, t] = sum_d dO[t, h, d] * O[t, h, d]
+template <int DH>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p, float* delta) {
+  constexpr int LP = DH / 8;
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
+  const int j = threadIdx.x % LP;
+  const int64_t total = (int64_t)p.B * p.L * p.h_q;
+  const bool valid = item < total;
+  const int64_t it = valid ? item : 0;
+  const int64_t tok = it / p.h_q;
+  const int head = (int)(it % p.h_q);
+  const u32x4_t a = ld16(p.dout + tok * p.lddo + (int64_t)head * DH + 8 * j);
+  const u32x4_t o = ld16(p.o + tok * p.ldo + (int64_t)head * DH + 8 * j);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += lo_f(a[e]) * lo_f(o[e]) + hi_f(a[e]) * hi_f(o[e]);
+  s = group_sum(s, LP);
+  if (valid && j == 0) {
+    const int64_t b = tok / p.L, t = tok % p.L;
+    delta[(b * p.h_q + head) * p.L + t] = s;
+  }
+}
 
 // dK, dV for 128 keys of one kv head (32 per wave).  K and V of those keys
 // and double-buffered Q / dO tiles of QT queries sit in LDS in the layout
