@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq3layer.so")
 SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "norm.hip",
-           "attn_bf16.hip", "attn_f32.hip", "transpose.hip"]
+           "attn_bf16.hip", "attn_f32.hip", "transpose.hip", "swiglu.hip"]
 ARCH = "gfx950"
 # Per-source flags.  The attention kernels run softmax arithmetic on their
 # matrix-instruction results: keeping those accumulators in ordinary VGPRs

@@ -480,11 +480,12 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   }
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
   // feature counts; A/B activations with row strides lda/ldb).
+  // With a_done, A's transpose is already in tA.
   auto wgrad = [&](const void* A, int lda, int ma, const void* B, int ldb, int nb,
-                   Epilogue e) -> hipError_t {
+                   Epilogue e, bool a_done = false) -> hipError_t {
     GemmArgs g{};
     if (bt) {
-      hipError_t err = transpose_bf16(T, Tp, ma, A, lda, tA, Tp, s);
+      hipError_t err = a_done ? hipSuccess : transpose_bf16(T, Tp, ma, A, lda, tA, Tp, s);
       if (err != hipSuccess) return err;
       err = transpose_bf16(T, Tp, nb, B, ldb, tB, Tp, s);
       if (err != hipSuccess) return err;
@@ -501,19 +502,30 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     return gemm(dt, g, s);
   };
 
-  // Step 9 (down_proj): df = dy W_down, fused with the SwiGLU adjoint.
+  // Step 9 (down_proj): df = dy W_down.  fp32: fused with the SwiGLU adjoint
+  // in the GEMM epilogue.  bf16: df lands in the dg half of dgu, and after
+  // dW_down a separate pass turns it into dg | du, writing the transpose the
+  // gate/up weight gradient reads as well (an epilogue that reads g, u would
+  // hold the matrix cores idle while it waits on memory).
   {
     GemmArgs g{};
     g.a = kop(dy, m.d, T);
     g.b = bt ? kop(wt_down, m.d, m.ffn) : rop(w->down, m.ffn, m.ffn);
     g.M = T; g.N = m.ffn; g.K = m.d;
-    g.epi.kind = EPI_SILU_BWD;
-    g.epi.c = dgu; g.epi.ldc = 2 * (int64_t)m.ffn;
-    g.epi.r = gu; g.epi.ldr = 2 * (int64_t)m.ffn; g.epi.ffn = m.ffn;
+    if (bt) {
+      g.epi = epi_store(dgu, 2 * (int64_t)m.ffn, nullptr, 0);
+    } else {
+      g.epi.kind = EPI_SILU_BWD;
+      g.epi.c = dgu; g.epi.ldc = 2 * (int64_t)m.ffn;
+      g.epi.r = gu; g.epi.ldr = 2 * (int64_t)m.ffn; g.epi.ffn = m.ffn;
+    }
     Q3L_HIP(gemm(dt, g, s));
   }
   if (want_w)  // dW_down = dy^T f
     Q3L_HIP(wgrad(dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc)));
+  if (bt)
+    Q3L_HIP(swiglu_bwd_bf16(T, Tp, m.ffn, dgu, 2 * (int64_t)m.ffn, gu, 2 * (int64_t)m.ffn,
+                            dgu, 2 * (int64_t)m.ffn, tA, Tp, s));
   // Step 9 (gate/up): dhn = dg W_gate + du W_up (one GEMM over stacked K).
   {
     GemmArgs g{};
@@ -531,7 +543,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (want_w) {  // dW_gate | dW_up = [dg du]^T hn
     Epilogue e = epi_wgrad(grads->gate, m.d, acc);
     e.cs[1] = grads->up; e.cstart[1] = m.ffn; e.cnseg = 2;
-    Q3L_HIP(wgrad(dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e));
+    Q3L_HIP(wgrad(dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e, /*a_done=*/bt));
   }
   // Steps 8 and 10: post-attention RMSNorm adjoint plus the residual dy.
   {
