@@ -6,6 +6,8 @@
 // All of these are HBM-bound: each reads its inputs once and writes its
 // outputs once with 16-byte accesses; reductions over a row stay inside a
 // wave64 (shuffles), reductions over rows go through per-block partial sums.
+#include <type_traits>
+
 #include "common.h"
 #include "ops.h"
 
@@ -157,7 +159,122 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   for (int i = threadIdx.x; i < n; i += 256) wpart[(int64_t)blockIdx.x * n + i] = sdw[i];
 }
 
-constexpr int kNormBwdParts = 256;
+// bf16 form of the same: a row's dy and x chunks are loaded once, all up
+// front, and kept packed in registers across the reduction; w stays in
+// registers for every row.  Residual bf16 (resid_f32 = 0) or fp32.
+template <int CPL>
+__global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
+    int64_t rows, int n, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ x,
+    const float* __restrict__ rstd, const bf16_t* __restrict__ w,
+    const void* __restrict__ resid, int resid_f32, bf16_t* __restrict__ dx,
+    float* __restrict__ dx32, float* __restrict__ wpart) {
+  extern __shared__ float sdw[];  // [n] dw partial, then w as bf16 [n]
+  bf16_t* sw = reinterpret_cast<bf16_t*>(sdw + n);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // 8 waves
+  const int nc = n / 8;
+  for (int i = threadIdx.x; i < n; i += 512) sdw[i] = 0.f;
+  for (int i = threadIdx.x; i < nc; i += 512) st16(sw + 8 * i, ld16(w + 8 * i));
+  float acc[CPL][8];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
+  __syncthreads();
+
+  const int64_t nwaves = (int64_t)gridDim.x * 8;
+  for (int64_t row = (int64_t)blockIdx.x * 8 + wave; row < rows; row += nwaves) {
+    // w is re-read from LDS for every row (a compiler barrier keeps its
+    // unpacked copy from being held in registers across rows).
+    asm volatile("" ::: "memory");
+    const float r = rstd[row];
+    u32x4_t ar[CPL], br[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        ar[c] = ld16(dy + row * n + 8 * ch);
+        br[c] = ld16(x + row * n + 8 * ch);
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if (lane + 64 * c < nc) {
+        const u32x4_t wv = ld16(sw + 8 * (lane + 64 * c));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pa = ar[c][j >> 1], pb = br[c][j >> 1], pw = wv[j >> 1];
+          const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
+          const float xh = ((j & 1) ? hi_f(pb) : lo_f(pb)) * r;
+          const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
+          dot += a * ww * xh;
+          acc[c][j] += a * xh;
+        }
+      }
+    }
+    // Unpacked copies of dy and x are not kept past the reduction (the empty
+    // asm marks the packed registers as rewritten): half the registers.
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) asm volatile("" : "+v"(ar[c]), "+v"(br[c]));
+    dot = wave_sum(dot) / (float)n;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        float rr[8];
+        if (resid_f32) {
+          const float* rp = static_cast<const float*>(resid) + row * n + 8 * ch;
+          const f32x4_t u = *reinterpret_cast<const f32x4_t*>(rp);
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(rp + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { rr[j] = u[j]; rr[4 + j] = v[j]; }
+        } else if (resid) {
+          const u32x4_t v = ld16(static_cast<const bf16_t*>(resid) + row * n + 8 * ch);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { rr[2 * j] = lo_f(v[j]); rr[2 * j + 1] = hi_f(v[j]); }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rr[j] = 0.f;
+        }
+        const u32x4_t wv = ld16(sw + 8 * ch);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pa = ar[c][j >> 1], pb = br[c][j >> 1], pw = wv[j >> 1];
+          const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
+          const float b = (j & 1) ? hi_f(pb) : lo_f(pb);
+          const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
+          o[j] = r * (a * ww - b * r * dot) + rr[j];
+        }
+        if (dx)
+          st16(dx + row * n + 8 * ch, u32x4_t{pack2(o[0], o[1]), pack2(o[2], o[3]),
+                                               pack2(o[4], o[5]), pack2(o[6], o[7])});
+        if (dx32) {
+          float* q = dx32 + row * n + 8 * ch;
+          *reinterpret_cast<f32x4_t*>(q) = f32x4_t{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4_t*>(q + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+        }
+      }
+    }
+  }
+  // Waves add their partials one after another: a fixed summation order, so
+  // the weight gradient is bitwise reproducible.
+  for (int wv = 0; wv < 8; ++wv) {
+    if (wave == wv) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nc)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sdw[8 * ch + j] += acc[c][j];
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < n; i += 512) wpart[(int64_t)blockIdx.x * n + i] = sdw[i];
+}
+
+constexpr int kNormBwdParts = 512;
 
 // ---- column reduction of partial rows -------------------------------------
 // A workgroup owns 64 columns; its 4 waves sum interleaved quarters of the
@@ -361,11 +478,30 @@ hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
                          int resid_f32, void* dx, float* dx32, float* wpart,
                          int* nparts, hipStream_t s) {
   const int cpl = (int)cdiv(n, 512);
-  int64_t grid = cdiv(rows, 4 * 8);  // at least 8 rows per wave
+  int64_t grid = cdiv(rows, 4 * 4);  // at least 4 rows per wave
   if (grid > kNormBwdParts) grid = kNormBwdParts;
   if (grid < 1) grid = 1;
   *nparts = (int)grid;
   const size_t shm = (size_t)n * sizeof(float);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    grid = cdiv(rows, 8 * 4);  // 8 waves per workgroup, at least 4 rows per wave
+    if (grid > kNormBwdParts) grid = kNormBwdParts;
+    if (grid < 1) grid = 1;
+    *nparts = (int)grid;
+#define Q3L_RB16(C)                                                                \
+  hipLaunchKernelGGL((rmsnorm_bwd_bf16_kernel<C>), dim3(grid), dim3(512),          \
+                     shm + (size_t)n * 2, s,                                       \
+                     rows, n, (const bf16_t*)dy, (const bf16_t*)x, rstd,           \
+                     (const bf16_t*)w, resid, resid_f32, (bf16_t*)dx, dx32, wpart)
+    if (cpl <= 1) Q3L_RB16(1);
+    else if (cpl <= 2) Q3L_RB16(2);
+    else if (cpl <= 4) Q3L_RB16(4);
+    else if (cpl <= 8) Q3L_RB16(8);
+    else if (cpl <= 16) Q3L_RB16(16);
+    else return hipErrorInvalidValue;
+#undef Q3L_RB16
+    return hipGetLastError();
+  }
 #define Q3L_RB(C)                                                              \
   hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, C>), dim3(grid), dim3(256), shm, s, \
                      rows, n, (const T*)dy, (const T*)x, rstd, (const T*)w,    \
