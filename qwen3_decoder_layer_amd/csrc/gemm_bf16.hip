@@ -282,8 +282,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   map_tile(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  OpSel<BM, TM, KB, NW, AK> oa;
-  OpSel<BN, TN, KB, NW, BKC> ob;
+  // With 8 waves only the first 4 (one per SIMD) issue the global->LDS
+  // loads: a wave blocks while its load instructions queue at the address
+  // unit, and the other wave on the same SIMD keeps the matrix core fed.
+  constexpr int NL = NW >= 8 ? NW / 2 : NW;    // waves that issue the loads
+  OpSel<BM, TM, KB, NL, AK> oa;
+  OpSel<BN, TN, KB, NL, BKC> ob;
   constexpr int LOADS = decltype(oa.ld)::NI + decltype(ob.ld)::NI;  // per slab
   oa.ld.init(g.a, m0, g.K, wave, lane);
   ob.ld.init(g.b, n0, g.K, wave, lane);
@@ -311,6 +315,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   // Part `part` (of SP) of slab kt's requests into stage dst.
   auto issue_part = [&](int kt, Q3L_LDS char* dst, int part) {
     const bool last = kt == klast;
+    if (wave >= NL) return;
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       if (q / NV != part) continue;
