@@ -299,18 +299,21 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p, float* de
   }
 }
 
-// dK, dV for 128 keys of one kv head (32 per wave).  K and V of those keys
-// and double-buffered Q / dO tiles of QT queries sit in LDS in the layout
-// above, filled by direct global->LDS loads (no registers, no LDS store
-// instructions); the transposed operands of dV^T += dO^T P^T and
-// dK^T += Q^T dS^T come from transposing LDS reads of the same tiles.
+// dK, dV for 128 keys of one kv head.  Eight waves: wave w owns keys
+// 32 (w % 4) .. +31 and, of every QT-query tile, the 32 query rows
+// 32 (w / 4) .. +31, so the two waves sharing a SIMD work on independent
+// halves of a tile and hide each other's latencies; their dK/dV partial sums
+// are added through LDS at the end.  K and V of the workgroup's keys and
+// double-buffered Q / dO tiles sit in LDS in the layout above, filled by
+// direct global->LDS loads (no registers, no LDS store instructions); the
+// transposed operands of dV^T += dO^T P^T and dK^T += Q^T dS^T come from
+// transposing LDS reads of the same tiles.
 template <int DH>
-__global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
+__global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   constexpr int NKK = DH / 16, NDT = DH / 32;
   constexpr int QT = 64, KB = 128;             // queries per tile, keys per workgroup
   constexpr int RB = 2 * DH;                   // bytes per row
   constexpr int CPR = RB / 16;                 // 16-byte chunks per row
-  constexpr int RPI = 1024 / RB;               // rows per direct-load instruction
   constexpr int KVB = KB * RB, TB = QT * RB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * KVB + 4 * TB];
   __shared__ __attribute__((aligned(16))) float sLD[2][2][QT];   // [stage][lse, delta][q]
@@ -321,10 +324,11 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (int)uni((uint32_t)(tid >> 6));
+  const int wk = wave & 3, half = wave >> 2;   // key block, query half
   const int l32 = lane & 31, h = lane >> 5;
   const int b = blockIdx.x / p.h_kv, kvh = blockIdx.x % p.h_kv;
   const int kb0 = blockIdx.y * KB;
-  const int kw0 = kb0 + 32 * wave;        // first key of this wave
+  const int kw0 = kb0 + 32 * wk;          // first key of this wave
   const int L = p.L;
   const int64_t tok0 = (int64_t)b * L;
   const int mykv = kw0 + l32;
@@ -338,8 +342,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
   auto load_tile = [&](int it, int s) {
     const int head = kvh * p.G + it / nqt;
     const int q0 = (qt_first + it % nqt) * QT;
-    load_rows_lds<DH, QT, 4>(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave, lane);
-    load_rows_lds<DH, QT, 4>(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave, lane);
+    load_rows_lds<DH, QT, 8>(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave, lane);
+    load_rows_lds<DH, QT, 8>(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave, lane);
     if (wave < 2) {   // log-sum-exp (wave 0) and row sums (wave 1), 64 floats each
       const float* src = wave == 0 ? (const float*)p.lse : p.delta;
       const int q = q0 + lane;
@@ -349,21 +353,22 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
     }
   };
 
-  load_rows_lds<DH, KB, 4>(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave, lane);
-  load_rows_lds<DH, KB, 4>(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave, lane);
+  load_rows_lds<DH, KB, 8>(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave, lane);
+  load_rows_lds<DH, KB, 8>(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave, lane);
   load_tile(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
 
-  // Per-lane LDS offsets.  16-byte reads (rows 32c + l32 of a Q/dO tile and
-  // rows 32 wave + l32 of K/V all share swz(l32)): chunk 2kk + h.
+  // Per-lane LDS offsets.  16-byte reads (rows 32 half + l32 of a Q/dO tile
+  // and rows 32 wk + l32 of K/V all share swz(l32)): chunk 2kk + h.
   uint32_t offq[NKK];
   {
     const int sw = swz<CPR>(l32);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) offq[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
   }
-  const uint32_t rowq = (uint32_t)l32 * RB, rowk = (uint32_t)(32 * wave + l32) * RB;
+  const uint32_t rowq = (uint32_t)(32 * half + l32) * RB;
+  const uint32_t rowk = (uint32_t)(32 * wk + l32) * RB;
   // Transposing reads for the dO^T / Q^T operands.
   TrOffsets<DH> tro;
   tro.init(lane);
@@ -377,57 +382,49 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
   for (int it = 0; it < total; ++it) {
     const int s = it & 1;
     if (it + 1 < total) load_tile(it + 1, s ^ 1);
-    const int q0 = (qt_first + it % nqt) * QT;
-    // Skip tiles entirely before this wave's keys (all masked).
-    if (q0 + QT - 1 >= kw0 && kw0 < L) {
+    const int qh0 = (qt_first + it % nqt) * QT + 32 * half;   // this wave's first row
+    // Skip row blocks entirely before this wave's keys (all masked).
+    if (qh0 + 31 >= kw0 && kw0 < L) {
       const Q3L_LDS char* sQ = stage(s);
       const Q3L_LDS char* sO = sQ + TB;
-      f32x16_t sc[2], dp[2];
+      f32x16_t sc, dp;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { sc[c][e] = 0.f; dp[c][e] = 0.f; }
+      for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const u32x4_t ka = ld_lds16(sK + rowk + offq[kk]);
         const u32x4_t va = ld_lds16(sV + rowk + offq[kk]);
+        sc = mfma32(ld_lds16(sQ + rowq + offq[kk]), ka, sc);
+        dp = mfma32(ld_lds16(sO + rowq + offq[kk]), va, dp);
+      }
+      // lane: key mykv; rows q = qh0 + 8(e/4) + 4h + e%4 -- four consecutive
+      // rows per e/4, so LSE and delta come in float4s.
+      const bool need_mask = (qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint32_t o = rowq + 32u * RB * c + offq[kk];
-          sc[c] = mfma32(ld_lds16(sQ + o), ka, sc[c]);
-          dp[c] = mfma32(ld_lds16(sO + o), va, dp[c]);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int qb = 32 * half + 8 * e4 + 4 * h;
+        const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qb]) * kLog2e;
+        const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qb]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * e4 + r;
+          float pv = exp2_raw(fmaf(sc[e], p.scale_log2, -lq[r]));
+          if (need_mask) {
+            const int q = qh0 + 8 * e4 + 4 * h + r;
+            if (mykv > q || q >= L || mykv >= L) pv = 0.f;
+          }
+          sc[e] = pv;
+          dp[e] = pv * (dp[e] - dq4[r]);
         }
       }
-      // lane: key mykv; rows q = q0 + 32c + 8(e/4) + 4h + e%4 -- four
-      // consecutive rows per (c, e/4), so LSE and delta come in float4s.
-      const bool need_mask = (q0 < kw0 + 31) || (q0 + QT > L) || (kw0 + 32 > L);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int qb = 32 * c + 8 * e4 + 4 * h;
-          const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qb]) * kLog2e;
-          const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qb]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * e4 + r;
-            float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, -lq[r]));
-            if (need_mask) {
-              const int q = q0 + qb + r;
-              if (mykv > q || q >= L || mykv >= L) pv = 0.f;
-            }
-            sc[c][e] = pv;
-            dp[c][e] = pv * (dp[c][e] - dq4[r]);
-          }
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pf = pack_half(sc[ks >> 1], ks & 1);
-        const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);
+      for (int hk = 0; hk < 2; ++hk) {
+        const u32x4_t pf = pack_half(sc, hk);
+        const u32x4_t df = pack_half(dp, hk);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          dvt[dt] = mfma32(tro.read(sO, ks, dt), pf, dvt[dt]);
-          dkt[dt] = mfma32(tro.read(sQ, ks, dt), df, dkt[dt]);
+          dvt[dt] = mfma32(tro.read(sO, 2 * half + hk, dt), pf, dvt[dt]);
+          dkt[dt] = mfma32(tro.read(sQ, 2 * half + hk, dt), df, dkt[dt]);
         }
       }
     }
@@ -435,7 +432,28 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(const FwdP p) {
     stage_barrier();      // everyone's part; stage s fully read
   }
 
-  if (mykv >= L) return;
+  // Waves 4..7 hand their partial sums to waves 0..3 through LDS (the
+  // stages are free now): per wave 2 NDT accumulators of 16 floats per lane.
+  float* red = (float*)smem;
+  constexpr int PW = 2 * NDT * 16 * 64;        // floats per wave
+  if (half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[wk * PW + ((2 * dt) * 16 + e) * 64 + lane] = dkt[dt][e];
+        red[wk * PW + ((2 * dt + 1) * 16 + e) * 64 + lane] = dvt[dt][e];
+      }
+  }
+  __syncthreads();
+  if (half == 1 || mykv >= L) return;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dkt[dt][e] += red[wk * PW + ((2 * dt) * 16 + e) * 64 + lane];
+      dvt[dt][e] += red[wk * PW + ((2 * dt + 1) * 16 + e) * 64 + lane];
+    }
   const float sc = p.scale_log2 / kLog2e;   // 1/sqrt(d_h)
   bf16_t* kp = p.dk + (tok0 + mykv) * p.ldk + (int64_t)kvh * DH;
   bf16_t* vp = p.dv + (tok0 + mykv) * p.ldv + (int64_t)kvh * DH;
@@ -621,11 +639,11 @@ hipError_t attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
   dim3 qgrid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
   if (a.d_h == 128) {
     hipLaunchKernelGGL(attn_delta_kernel<128>, dgrid, dim3(256), 0, s, p, a.delta);
-    hipLaunchKernelGGL(attn_dkdv_kernel<128>, kgrid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkdv_kernel<128>, kgrid, dim3(512), 0, s, p);
     hipLaunchKernelGGL(attn_dq_kernel<128>, qgrid, dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL(attn_delta_kernel<64>, dgrid, dim3(256), 0, s, p, a.delta);
-    hipLaunchKernelGGL(attn_dkdv_kernel<64>, kgrid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkdv_kernel<64>, kgrid, dim3(512), 0, s, p);
     hipLaunchKernelGGL(attn_dq_kernel<64>, qgrid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
