@@ -277,24 +277,26 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
 constexpr int kNormBwdParts = 512;
 
 // ---- column reduction of partial rows -------------------------------------
-// A workgroup owns 64 columns; its 4 waves sum interleaved quarters of the
-// partial rows (lanes over columns: 256-byte coalesced reads), then combine
-// in a fixed order.
-__global__ __launch_bounds__(256) void reduce_rows_kernel(
+// A workgroup owns 64 columns; its 16 waves sum interleaved sixteenths of
+// the partial rows (lanes over columns: 256-byte coalesced reads), then
+// combine in a fixed order.
+__global__ __launch_bounds__(1024) void reduce_rows_kernel(
     const float* __restrict__ part, int nparts, int n, float* __restrict__ out,
     int accumulate) {
-  __shared__ float red[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // 16 waves
   const int i = blockIdx.x * 64 + lane;
   float s = 0.f;
   if (i < n) {
 #pragma unroll 8
-    for (int p = wave; p < nparts; p += 4) s += part[(int64_t)p * n + i];
+    for (int p = wave; p < nparts; p += 16) s += part[(int64_t)p * n + i];
   }
   red[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && i < n) {
-    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += red[w][lane];
     out[i] = accumulate ? out[i] + t : t;
   }
 }
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
   }
 }
 
-constexpr int kQkBwdParts = 512;
+constexpr int kQkBwdParts = 1024;
 
 template <class T>
 hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
@@ -548,7 +550,7 @@ hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
 
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
                        int accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 64)), dim3(256),
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 64)), dim3(1024),
                      0, s, part, nparts, n, out, accumulate);
   return hipGetLastError();
 }
@@ -595,6 +597,8 @@ hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
   const int64_t tokens = (int64_t)B * L;
   const int64_t items = tokens * (h_q + h_kv);
   const int per_block = 256 / (d_h / 8);
+  // Many small workgroups (enough waves to keep the loads in flight); each
+  // writes one partial row of the q/k norm weight gradients.
   int64_t grid = cdiv(items, (int64_t)per_block * 8);
   if (grid > kQkBwdParts) grid = kQkBwdParts;
   if (grid < 1) grid = 1;
