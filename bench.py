@@ -41,10 +41,10 @@ COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 # --kernel-probe`, each scaled by what the same counter reads for the 1 GiB
 # calibration copy.  Valid only for the kernel source it was taken on: the
 # digest below is of gemm_bf16.hip, and a changed source reports null.
-TRAFFIC = {"source_sha256": "299afac95d2718a9",
-           "fetch_kib": 1179986.3, "write_kib": 682967.7,
-           "copy_fetch_kib": 524303.1, "copy_write_kib": 1048576.0,
-           "bytes": 3115901268}
+TRAFFIC = {"source_sha256": "d9246e0f8e8a13c7",
+           "fetch_kib": 1194045.4, "write_kib": 674846.1,
+           "copy_fetch_kib": 524302.2, "copy_write_kib": 1048576.0,
+           "bytes": 3136381317}
 
 WORKLOADS = {
     "qwen3-8b-bf16-fwd-bwd": 4,
