@@ -193,11 +193,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   load_tile(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
-  for (int t = 0; t < ntiles; ++t) {
-    const int s = t & 1;
+  // One K/V tile; the stage index is a compile-time constant (the loop runs
+  // two tiles per trip), so LDS addresses are a per-lane register plus an
+  // immediate offset and need no per-tile arithmetic.
+  auto tile = [&](int t, auto stage_c) {
+    constexpr int s = decltype(stage_c)::value;
     if (t + 1 < ntiles) load_tile(t + 1, s ^ 1);
     if (t < my_tiles) {
-      const Q3L_LDS char* sK = stage(s);
+      const Q3L_LDS char* sK = lds + s * 2 * TB;
       const Q3L_LDS char* sV = sK + TB;
       const int kv0 = t * KT;
       f32x16_t sc[2];
@@ -258,6 +261,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     }
     wait_vmcnt<0>();
     stage_barrier();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (qrow >= L) return;
