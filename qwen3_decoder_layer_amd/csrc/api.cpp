@@ -95,6 +95,11 @@ q3l_status validate(const q3l_layer_cfg* c) {
     if ((T + 8) * widest_act * 2 >= (1LL << 31))
       return fail(Q3L_EUNSUPPORTED, "B*L=%lld tokens x %lld features exceeds 2 GiB per "
                   "activation tensor", (long long)T, (long long)widest_act);
+    const int64_t wmax = std::max<int64_t>((int64_t)c->d_ffn,
+                                           (int64_t)(c->h_q + 2 * c->h_kv) * c->d_h);
+    if ((wmax + 8) * c->d * 2 >= (1LL << 31))
+      return fail(Q3L_EUNSUPPORTED, "a %lld x %d weight exceeds 2 GiB", (long long)wmax,
+                  c->d);
   }
   return Q3L_OK;
 }

@@ -92,11 +92,25 @@ def test_validate_accepts_the_workload_shapes(abi, lib):
     ("qk_norm", 2, 1),
     ("dtype", 7, 1),
     ("L", -1, 1),
+    ("L", 0, 1),             # empty sequence
+    ("B", 0, 1),             # empty batch
 ])
 def test_validate_rejects(abi, lib, field, value, status):
     cfg = cfg_of(abi, **{field: value})
     assert lib.q3l_validate(C.byref(cfg)) == status
     assert len(err(lib)) > 5
+
+
+def test_validate_rejects_tensors_past_the_32bit_offset_range(abi, lib):
+    # bf16 activations are addressed with 32-bit byte offsets: 2^31 bytes and
+    # up are refused before anything runs; fp32 (plain kernels) is not bound.
+    big = cfg_of(abi, d=4096, d_ffn=12288, B=16, L=65536)
+    assert lib.q3l_validate(C.byref(big)) == 2
+    assert "2 GiB" in err(lib)
+    wide = cfg_of(abi, d=8192, d_ffn=131072, B=1, L=16)
+    assert lib.q3l_validate(C.byref(wide)) == 2
+    ok = cfg_of(abi, d=4096, d_ffn=12288, B=2, L=4096)
+    assert lib.q3l_validate(C.byref(ok)) == 0
 
 
 def test_validate_null_cfg(abi, lib):
