@@ -130,9 +130,9 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
 
 struct BwdWs {
   size_t dgu, dhn, dh32, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
-  // bf16 only: transposed weights ([in, out]) and two scratch buffers for the
-  // transposed operands of the weight-gradient GEMMs ([features, Tp]).
-  size_t wt_down, wt_gu, wt_o, wt_qkv, tA, tB;
+  // bf16 only: transposed weights ([in, out]) and three scratch buffers for
+  // the transposed operands of the weight-gradient GEMMs ([features, Tp]).
+  size_t wt_down, wt_gu, wt_o, wt_qkv, tA, tB, tC;
   size_t total;
 };
 
@@ -163,6 +163,7 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
     w.wt_qkv = take((size_t)m.d * m.nqkv * 2);
     w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
     w.tB = take((size_t)std::max<int64_t>(std::max<int64_t>(m.ffn, m.qd), m.d) * Tp * 2);
+    w.tC = take((size_t)m.d * Tp * 2);
   }
   w.total = off;
   return w;
@@ -462,7 +463,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   // bf16: every backward GEMM runs in the matrix-core kernel's K-contiguous
   // form.  Weights are transposed to [in, out] once per call; the two
   // operands of each weight-gradient GEMM are transposed to [features, T]
-  // (T padded to a multiple of 8 with zeros) into two reused scratch buffers.
+  // (T padded to a multiple of 8 with zeros) into reused scratch buffers.
   const bool bt = dt == Q3L_BF16;
   const int Tp = (int)pad8(m.T);
   char* wt_down = bt ? at(workspace, W.wt_down) : nullptr;
@@ -471,6 +472,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   char* wt_qkv = bt ? at(workspace, W.wt_qkv) : nullptr;
   char* tA = bt ? at(workspace, W.tA) : nullptr;
   char* tB = bt ? at(workspace, W.tB) : nullptr;
+  char* tC = bt ? at(workspace, W.tC) : nullptr;
   if (bt) {
     Q3L_HIP(transpose_bf16(m.d, m.d, m.ffn, w->down, m.ffn, wt_down, m.d, s));
     Q3L_HIP(transpose_bf16(m.ffn, m.ffn, m.d, w->gate, m.d, wt_gu, 2 * m.ffn, s));
@@ -484,18 +486,22 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
                            wt_qkv + (size_t)(m.qd + m.kvd) * 2, m.nqkv, s));
   }
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
-  // feature counts; A/B activations with row strides lda/ldb).
-  // With a_done, A's transpose is already in tA.
+  // feature counts; A/B activations with row strides lda/ldb).  bf16: A and
+  // B are transposed into tA and tB (tA_, tB_ when given); a_done / b_done
+  // say that transpose is already there.
   auto wgrad = [&](const void* A, int lda, int ma, const void* B, int ldb, int nb,
-                   Epilogue e, bool a_done = false) -> hipError_t {
+                   Epilogue e, bool a_done = false, bool b_done = false,
+                   char* tA_ = nullptr, char* tB_ = nullptr) -> hipError_t {
     GemmArgs g{};
     if (bt) {
-      hipError_t err = a_done ? hipSuccess : transpose_bf16(T, Tp, ma, A, lda, tA, Tp, s);
+      char* ta = tA_ ? tA_ : tA;
+      char* tb = tB_ ? tB_ : tB;
+      hipError_t err = a_done ? hipSuccess : transpose_bf16(T, Tp, ma, A, lda, ta, Tp, s);
       if (err != hipSuccess) return err;
-      err = transpose_bf16(T, Tp, nb, B, ldb, tB, Tp, s);
+      err = b_done ? hipSuccess : transpose_bf16(T, Tp, nb, B, ldb, tb, Tp, s);
       if (err != hipSuccess) return err;
-      g.a = kop(tA, Tp, ma);
-      g.b = kop(tB, Tp, nb);
+      g.a = kop(ta, Tp, ma);
+      g.b = kop(tb, Tp, nb);
       g.K = Tp;
     } else {
       g.a = rop(A, lda, ma);
@@ -508,10 +514,10 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   };
 
   // Step 9 (down_proj): df = dy W_down.  fp32: fused with the SwiGLU adjoint
-  // in the GEMM epilogue.  bf16: df lands in the dg half of dgu, and after
-  // dW_down a separate pass turns it into dg | du, writing the transpose the
-  // gate/up weight gradient reads as well (an epilogue that reads g, u would
-  // hold the matrix cores idle while it waits on memory).
+  // in the GEMM epilogue.  bf16: df lands in the dg half of dgu, and a
+  // separate pass turns it into dg | du, writing the transposes the two
+  // weight gradients read as well: [dg du]^T and f^T (an epilogue that reads
+  // g, u would hold the matrix cores idle while it waits on memory).
   {
     GemmArgs g{};
     g.a = kop(dy, m.d, T);
@@ -526,11 +532,13 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     }
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (want_w)  // dW_down = dy^T f
-    Q3L_HIP(wgrad(dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc)));
   if (bt)
     Q3L_HIP(swiglu_bwd_bf16(T, Tp, m.ffn, dgu, 2 * (int64_t)m.ffn, gu, 2 * (int64_t)m.ffn,
-                            dgu, 2 * (int64_t)m.ffn, tA, Tp, s));
+                            dgu, 2 * (int64_t)m.ffn, want_w ? tA : nullptr, Tp,
+                            want_w ? tB : nullptr, s));
+  if (want_w)  // dW_down = dy^T f  (bf16: f^T already in tB)
+    Q3L_HIP(wgrad(dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc),
+                  /*a_done=*/false, /*b_done=*/bt, tC, nullptr));
   // Step 9 (gate/up): dhn = dg W_gate + du W_up (one GEMM over stacked K).
   {
     GemmArgs g{};

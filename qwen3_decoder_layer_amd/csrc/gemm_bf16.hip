@@ -4,7 +4,8 @@
 //
 // C[M, N] = sum_k A(m, k) B(n, k), fp32 accumulation.
 //
-// Design (one workgroup = 4 wave64s = one BM x BN output tile):
+// Design (one workgroup = one BM x BN output tile; 256 x 256 with 8 wave64s
+// for the layer's large GEMMs, 4 wave64s for smaller tiles):
 //  - K is consumed in slabs of KB (64).  A K-contiguous operand (activations
 //    [T, f], weights [out, in]) goes from HBM straight into LDS with buffer
 //    loads (buffer_load_dwordx4 ... lds): no staging registers, no LDS store
@@ -25,8 +26,11 @@
 //    while the matrix cores work on the current one; one barrier per slab.
 //    Within a slab the next k-step's fragment reads are interleaved with
 //    the current step's matrix instructions (scheduling-group barriers).
-//  - The waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile of
-//    32x32 accumulators (v_mfma_f32_32x32x16_bf16).  The B fragment is
+//  - The waves form a 2 x (NW/2) grid; each owns a (BM/2) x (2 BN/NW)
+//    sub-tile of 32x32 accumulators (v_mfma_f32_32x32x16_bf16): 128 x 64 at
+//    256 x 256 with 8 waves, two waves per SIMD so one's LDS reads and
+//    barrier waits hide behind the other's matrix instructions.  With 8
+//    waves only the first 4 issue the direct loads.  The B fragment is
 //    passed as the MFMA's first operand so each lane ends up holding four
 //    consecutive output columns of one row: epilogue stores are 8 or 16
 //    bytes wide.

@@ -72,12 +72,13 @@ hipError_t transpose_bf16(int rows, int rows_pad, int cols, const void* src,
                           int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s);
 
 // SwiGLU adjoint, bf16: from df [T, ffn] and the saved g|u [T, 2 ffn] write
-// dgu = [dg | du] ([T, 2 ffn]) and its transpose dguT ([2 ffn, Tp], columns
-// t >= T zero).  df may alias the dg half of dgu (same ld).  ffn and Tp
-// multiples of 8.
+// dgu = [dg | du] ([T, 2 ffn]) and, if dguT is not null, its transpose dguT
+// ([2 ffn, Tp], columns t >= T zero).  If fT is not null, also writes fT = (silu(g) u)^T
+// ([ffn, Tp], same ld_t, columns t >= T zero).  df may alias the dg half of
+// dgu (same ld).  ffn and Tp multiples of 8.
 hipError_t swiglu_bwd_bf16(int T, int Tp, int ffn, const void* df, int64_t ld_df,
                            const void* gu, int64_t ld_gu, void* dgu, int64_t ld_dgu,
-                           void* dguT, int64_t ld_t, hipStream_t s);
+                           void* dguT, int64_t ld_t, void* fT, hipStream_t s);
 
 // ---- norms / RoPE / elementwise (dtype: 0 fp32, 1 bf16) -------------------
 hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,

@@ -1,15 +1,17 @@
 // SwiGLU adjoint (walkthrough page, Step 9: f = silu(g) * u with
-// g = hn W_gate^T, u = hn W_up^T), bf16, fused with the transposed copy the
-// gate/up weight-gradient GEMM reads:
+// g = hn W_gate^T, u = hn W_up^T), bf16, fused with the transposed copies the
+// two MLP weight-gradient GEMMs read:
 //   dg = df * u * s * (1 + g (1 - s)),  du = df * g * s,   s = sigmoid(g)
-// written to dgu = [dg | du] ([T, 2 ffn], row-major) and to
-// dguT = [dg | du]^T ([2 ffn, Tp], columns t >= T zero).
+// written to dgu = [dg | du] ([T, 2 ffn], row-major) and, when asked, to
+// dguT = [dg | du]^T ([2 ffn, Tp]) and fT = (g * s * u)^T ([ffn, Tp]); the
+// transposed columns t >= T are zero.  f is recomputed from the saved g and u
+// instead of read back from the forward's copy.
 // HBM-bound: each lane moves one 8x8 block of df, g and u through registers
-// (16-byte loads), and writes its 8x8 blocks of dg and du twice, as rows and
-// (after an in-register transpose) as columns.  A wave covers 64 tokens x 64
-// features; every load and store instruction touches 128 contiguous bytes
-// per row.  dgu's dg half may hold df itself: each lane reads its df block
-// before writing the dg block at the same place.
+// (16-byte loads), and writes its 8x8 blocks of dg and du as rows and (after
+// an in-register transpose) as columns, plus f's block as columns.  A wave
+// covers 64 tokens x 64 features; every load and store instruction touches
+// 128 contiguous bytes per row.  dgu's dg half may hold df itself: each lane
+// reads its df block before writing the dg block at the same place.
 #include "common.h"
 #include "ops.h"
 
@@ -20,7 +22,7 @@ __device__ inline float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f +
 
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
     int T, int Tp, int ffn, const bf16_t* df, int64_t ld_df, const bf16_t* gu,
-    int64_t ld_gu, bf16_t* dgu, int64_t ld_dgu, bf16_t* dguT, int64_t ld_t) {
+    int64_t ld_gu, bf16_t* dgu, int64_t ld_dgu, bf16_t* dguT, int64_t ld_t, bf16_t* fT) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ntc = (ffn + 63) / 64;
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
     vg[r] = ok ? ld16(gu + t * ld_gu + f0) : u32x4_t{0u, 0u, 0u, 0u};
     vu[r] = ok ? ld16(gu + t * ld_gu + ffn + f0) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  u32x4_t og[8], ou[8];
+  u32x4_t og[8], ou[8], of[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -51,7 +53,14 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
       og[r][w] = pack2(d0 * u0 * s0 * (1.0f + g0 * (1.0f - s0)),
                        d1 * u1 * s1 * (1.0f + g1 * (1.0f - s1)));
       ou[r][w] = pack2(d0 * g0 * s0, d1 * g1 * s1);
+      of[r][w] = pack2(g0 * s0 * u0, g1 * s1 * u1);
     }
+  if (fT != nullptr) {
+    u32x4_t tf[8];
+    transpose8x8(of, tf);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st16(fT + (int64_t)(f0 + c) * ld_t + t0, tf[c]);
+  }
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int64_t t = t0 + r;
@@ -60,6 +69,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
       st16(dgu + t * ld_dgu + ffn + f0, ou[r]);
     }
   }
+  if (dguT == nullptr) return;
   u32x4_t tg[8], tu[8];
   transpose8x8(og, tg);
   transpose8x8(ou, tu);
@@ -74,12 +84,12 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(
 
 hipError_t swiglu_bwd_bf16(int T, int Tp, int ffn, const void* df, int64_t ld_df,
                            const void* gu, int64_t ld_gu, void* dgu, int64_t ld_dgu,
-                           void* dguT, int64_t ld_t, hipStream_t s) {
+                           void* dguT, int64_t ld_t, void* fT, hipStream_t s) {
   if (Tp <= 0 || ffn <= 0) return hipSuccess;
   const int64_t tiles = cdiv(Tp, 64) * cdiv(ffn, 64);
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)cdiv(tiles, 4)), dim3(256), 0, s,
                      T, Tp, ffn, (const bf16_t*)df, ld_df, (const bf16_t*)gu, ld_gu,
-                     (bf16_t*)dgu, ld_dgu, (bf16_t*)dguT, ld_t);
+                     (bf16_t*)dgu, ld_dgu, (bf16_t*)dguT, ld_t, (bf16_t*)fT);
   return hipGetLastError();
 }
 
