@@ -24,8 +24,9 @@
 //    by (r >> 1) & 7, so the 16-byte fragment reads of 16 consecutive rows
 //    hit 16 distinct bank groups.  Two LDS stages: the next slab streams in
 //    while the matrix cores work on the current one; one barrier per slab.
-//    Within a slab the next k-step's fragment reads are interleaved with
-//    the current step's matrix instructions (scheduling-group barriers).
+//    Within a slab each k-step is a fixed sequence of slots (a matrix
+//    instruction, one fragment read for the next step, a share of the
+//    requests), pinned with scheduling barriers.
 //  - The waves form a 2 x (NW/2) grid; each owns a (BM/2) x (2 BN/NW)
 //    sub-tile of 32x32 accumulators (v_mfma_f32_32x32x16_bf16): 128 x 64 at
 //    256 x 256 with 8 waves, two waves per SIMD so one's LDS reads and
@@ -40,6 +41,8 @@
 //  - Fused epilogues: residual add (Steps 7 and 10), fp32 partial output for
 //    a tensor-parallel share, silu(gate) * up over an interleaved gate/up
 //    operand (Step 9), the SwiGLU backward, and fp32 (+=) weight gradients.
+#include <type_traits>
+
 #include "common.h"
 #include "ops.h"
 
@@ -248,23 +251,6 @@ template <int ROWS, int TT, int KB, int NW> struct OpSel<ROWS, TT, KB, NW, false
 };
 
 
-// Scheduling groups for one k-step of NM matrix instructions: the NR LDS
-// fragment reads of the next step go out early (one after each of the first
-// matrix instructions, or spread evenly when there are more reads than
-// matrix instructions), and the NV global->LDS requests are spread evenly,
-// so the address FIFO never backs up into the matrix-instruction stream.
-template <int R, int NM, int NR, int NV>
-__device__ inline void sched_from() {
-  if constexpr (R < NM) {
-    constexpr int rd = NR > NM ? ((R + 1) * NR) / NM - (R * NR) / NM : (R < NR ? 1 : 0);
-    constexpr int vm = ((R + 1) * NV) / NM - (R * NV) / NM;
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, rd, 0);
-    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);
-    sched_from<R + 1, NM, NR, NV>();
-  }
-}
-
 // ---- the kernel -----------------------------------------------------------
 // NS LDS stages of KB-deep slabs: slab kt+NS-1 is requested while slab kt is
 // multiplied, so global latency is hidden behind NS-1 slabs of MFMA work.
@@ -275,7 +261,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int ABYTES = BM * KB * 2, BBYTES = BN * KB * 2;
   constexpr int STAGE = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  // The epilogue reuses the LDS: per wave, half its rows of fp32 results
+  // (rows padded by 16 bytes).
+  constexpr int ERS = (BN / (NW / 2)) * 4 + 16;      // staged row, bytes
+  constexpr int EREG = (BM / 4) * ERS;                // per wave
+  constexpr int SMEM = NS * STAGE > NW * EREG ? NS * STAGE : NW * EREG;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -314,52 +305,65 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   constexpr int NIA = decltype(oa.ld)::NI;
   static_assert(LOADS % SP == 0, "requests split evenly over the steps");
   constexpr int NV = LOADS / SP;               // requests per k-step
+  constexpr int NF = TM + TN;                  // fragment reads per k-step
+  constexpr int NM = TM * TN;                  // matrix instructions per k-step
+  static_assert(NF <= NM, "one fragment read per matrix-instruction slot");
   const int nk = (g.K + KB - 1) / KB;
   const int klast = nk - 1;
-  // Part `part` (of SP) of slab kt's requests into stage dst.
-  auto issue_part = [&](int kt, Q3L_LDS char* dst, int part) {
+  // Requests q0 .. q1-1 (of LOADS) of slab kt into stage dst.
+  auto issue = [&](int kt, Q3L_LDS char* dst, int q0, int q1) __attribute__((always_inline)) {
     const bool last = kt == klast;
-    if (wave >= NL) return;
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
-      if (q / NV != part) continue;
+      if (q < q0 || q >= q1) continue;
       if (q < NIA)
         oa.ld.issue_one(g.a, q, kt * KB, g.K, last, dst, wave);
       else
         ob.ld.issue_one(g.b, q - NIA, kt * KB, g.K, last, dst + ABYTES, wave);
     }
   };
-  // Fragment reads in the order the matrix instructions consume them
-  // (row-major over the TM x TN accumulators): a0, b0 .. b{TN-1}, a1 ..
-  auto frags = [&](const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk,
-                   u32x4_t (&af)[TM], u32x4_t (&bf)[TN]) {
-    af[0] = oa.fr.read(As, kk, 0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = ob.fr.read(Bs, kk, j);
-#pragma unroll
-    for (int i = 1; i < TM; ++i) af[i] = oa.fr.read(As, kk, i);
+  // Fragment read x of a k-step, in the order the matrix instructions
+  // consume them (row-major over the TM x TN accumulators): a0, b0 ..
+  // b{TN-1}, a1 .. a{TM-1}.
+  auto frag = [&](const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk, int x,
+                  u32x4_t (&af)[TM], u32x4_t (&bf)[TN]) __attribute__((always_inline)) {
+    if (x == 0)
+      af[0] = oa.fr.read(As, kk, 0);
+    else if (x <= TN)
+      bf[x - 1] = ob.fr.read(Bs, kk, x - 1);
+    else
+      af[x - TN] = oa.fr.read(As, kk, x - TN);
   };
-  auto mma = [&](const u32x4_t (&af)[TM], const u32x4_t (&bf)[TN]) {
+  // One k-step in a fixed order of NM slots: slot x holds matrix
+  // instruction x, then (if rd) fragment read x of the next step, then (if
+  // ld) the x-th share of request part `part`.  Nothing moves across slots:
+  // a request stalled at the address unit delays only what follows it, and
+  // the other wave on the SIMD keeps the matrix core busy meanwhile.
+  auto step = [&](const u32x4_t (&ca)[TM], const u32x4_t (&cb)[TN], bool rd,
+                  const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk,
+                  u32x4_t (&na)[TM], u32x4_t (&nb)[TN], bool ld, int kt,
+                  Q3L_LDS char* dst, int part) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bf[j], af[i], acc[i][j]);
+    for (int x = 0; x < NM; ++x) {
+      acc[x / TN][x % TN] = mfma32(cb[x % TN], ca[x / TN], acc[x / TN][x % TN]);
+      if (rd && x < NF) frag(As, Bs, kk, x, na, nb);
+      if (ld) issue(kt, dst, part * NV + x * NV / NM, part * NV + (x + 1) * NV / NM);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // A K-contiguous fragment is one LDS read, a transposed one two.
-  constexpr int NR = (AK ? TM : 2 * TM) + (BKC ? TN : 2 * TN);
-  constexpr int NM = TM * TN;
 
   // Slab kt lives in stage kt % NS.  All stages start filling at once.
+  if (wave < NL) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-#pragma unroll
-    for (int part = 0; part < SP; ++part) issue_part(min(st, klast), lds + st * STAGE, part);
+    for (int st = 0; st < NS; ++st) issue(min(st, klast), lds + st * STAGE, 0, LOADS);
+  }
   wait_vmcnt<LOADS * (NS - 1)>();
   stage_barrier();
   // Fragments are double-buffered in registers: while the matrix cores work
   // on k-step kk, the reads for step kk+1 are in flight.
   u32x4_t af[2][TM], bfr[2][TN];
-  frags(lds, lds + ABYTES, 0, af[0], bfr[0]);
+#pragma unroll
+  for (int x = 0; x < NF; ++x) frag(lds, lds + ABYTES, 0, x, af[0], bfr[0]);
 
   // The stage barrier sits before the LAST k-step of a slab, whose fragments
   // are already in registers: after it the next slab's first fragments are
@@ -369,134 +373,161 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   // of slab kt+1; NS-2 younger slabs stay in flight.  Requests past the last
   // slab repeat it into stages nothing reads any more (in the first
   // iteration the pending parts repeat slab NS-1 into its own stage: the
-  // same bytes).
-  int cur = 0;
-  int pend = min(NS - 1, klast);
-  Q3L_LDS char* pend_dst = lds + (NS - 1) * STAGE;
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    const int nxt = cur + 1 == NS ? 0 : cur + 1;
-    Q3L_LDS char* As = lds + cur * STAGE;
-    const Q3L_LDS char* Bs = As + ABYTES;
+  // same bytes).  Loader and non-loader waves run separate copies of the
+  // loop, so neither has a branch around the requests.
+  auto main_loop = [&](auto loader) __attribute__((always_inline)) {
+    constexpr bool LD = decltype(loader)::value;
+    int cur = 0;
+    int pend = min(NS - 1, klast);
+    Q3L_LDS char* pend_dst = lds + (NS - 1) * STAGE;
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      const int nxt = cur + 1 == NS ? 0 : cur + 1;
+      Q3L_LDS char* As = lds + cur * STAGE;
+      const Q3L_LDS char* Bs = As + ABYTES;
 #pragma unroll
-    for (int kk = 0; kk < KS - 1; ++kk) {
-      frags(As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
-      if (kk + 1 < SP) issue_part(pend, pend_dst, kk + 1);
-      mma(af[kk & 1], bfr[kk & 1]);
-      if (kk + 1 < SP)
-        sched_from<0, NM, NR, NV>();
-      else
-        sched_from<0, NM, NR, 0>();
+      for (int kk = 0; kk < KS - 1; ++kk)
+        step(af[kk & 1], bfr[kk & 1], true, As, Bs, kk + 1, af[(kk + 1) & 1],
+             bfr[(kk + 1) & 1], LD && kk + 1 < SP, pend, pend_dst, kk + 1);
+      wait_vmcnt<LOADS * (NS - 2)>();
+      stage_barrier();
+      const Q3L_LDS char* Nx = lds + nxt * STAGE;
+      pend = min(kt + NS, klast);
+      pend_dst = As;
+      step(af[(KS - 1) & 1], bfr[(KS - 1) & 1], true, Nx, Nx + ABYTES, 0, af[0], bfr[0], LD,
+           pend, pend_dst, 0);
+      cur = nxt;
     }
-    wait_vmcnt<LOADS * (NS - 2)>();
-    stage_barrier();
-    const Q3L_LDS char* Nx = lds + nxt * STAGE;
-    frags(Nx, Nx + ABYTES, 0, af[0], bfr[0]);
-    pend = min(kt + NS, klast);
-    pend_dst = As;
-    issue_part(pend, pend_dst, 0);
-    mma(af[(KS - 1) & 1], bfr[(KS - 1) & 1]);
-    sched_from<0, NM, NR, NV>();
-    cur = nxt;
-  }
-  {
     const Q3L_LDS char* As = lds + cur * STAGE;
     const Q3L_LDS char* Bs = As + ABYTES;
 #pragma unroll
-    for (int kk = 0; kk < KS - 1; ++kk) {
-      frags(As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
-      mma(af[kk & 1], bfr[kk & 1]);
-      sched_from<0, NM, NR, 0>();
-    }
-    mma(af[(KS - 1) & 1], bfr[(KS - 1) & 1]);
-  }
+    for (int kk = 0; kk < KS - 1; ++kk)
+      step(af[kk & 1], bfr[kk & 1], true, As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1],
+           false, 0, nullptr, 0);
+    step(af[(KS - 1) & 1], bfr[(KS - 1) & 1], false, As, Bs, 0, af[0], bfr[0], false, 0,
+         nullptr, 0);
+  };
+  if (wave < NL)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   // The last requests (repeats of the final slab into idle stages) must
   // land before the workgroup's LDS is released.
   wait_vmcnt<0>();
 
-  // ---- epilogue: lane holds C[m][n..n+3] for each (i, j, q) ----
+  // ---- epilogue ----
+  // Lane holds C[m][n..n+3] for each (i, j, q): m = i*32 + lane%32 and
+  // n = j*32 + 8q + 4*(lane/32) within the wave's WM x WN sub-tile.
   const Epilogue& e = g.epi;
   const int hl = 4 * (lane >> 5);
+  if constexpr (EPI == EPI_SILU_BWD) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + (lane & 31);
-    if (m >= g.M) continue;
-    if constexpr (EPI == EPI_SILU_MUL) {
-#pragma unroll
-      for (int j = 0; j < TN; j += 2) {
-        const int fbase = (n0 + wn * WN) / 2 + (j / 2) * 32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = fbase + 8 * q + hl;
-          if (f >= e.ffn) continue;
-          float gv[4], uv[4], fv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            gv[r] = acc[i][j][4 * q + r];
-            uv[r] = acc[i][j + 1][4 * q + r];
-            fv[r] = silu_f(gv[r]) * uv[r];
-          }
-          bf16_t* F = static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + f;
-          st8(F, u32x2_t{pack2(fv[0], fv[1]), pack2(fv[2], fv[3])});
-          if (e.gu) {
-            bf16_t* G = static_cast<bf16_t*>(e.gu) + (int64_t)m * e.ldgu + f;
-            st8(G, u32x2_t{pack2(gv[0], gv[1]), pack2(gv[2], gv[3])});
-            st8(G + e.ffn, u32x2_t{pack2(uv[0], uv[1]), pack2(uv[2], uv[3])});
-          }
-        }
-      }
-    } else {
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * WM + i * 32 + (lane & 31);
+      if (m >= g.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + wn * WN + j * 32 + 8 * q + hl;
           if (n >= g.N) continue;
-          float v[4];
+          const bf16_t* G = static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n;
+          const u32x2_t g2 = ld8(G), u2 = ld8(G + e.ffn);
+          const float gg[4] = {lo_f(g2[0]), hi_f(g2[0]), lo_f(g2[1]), hi_f(g2[1])};
+          const float uu[4] = {lo_f(u2[0]), hi_f(u2[0]), lo_f(u2[1]), hi_f(u2[1])};
+          float dg[4], du[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+          for (int r = 0; r < 4; ++r) {
+            const float v = acc[i][j][4 * q + r];
+            const float sg = sigmoid_f(gg[r]);
+            dg[r] = v * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
+            du[r] = v * gg[r] * sg;
+          }
+          bf16_t* D = static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n;
+          st8(D, u32x2_t{pack2(dg[0], dg[1]), pack2(dg[2], dg[3])});
+          st8(D + e.ffn, u32x2_t{pack2(du[0], du[1]), pack2(du[2], du[3])});
+        }
+      }
+    }
+  } else {
+    // Staged through LDS: once every wave is past its last fragment read,
+    // each wave writes half of its fp32 sub-tile at a time into its own LDS
+    // region and reads it back row-major, so every global access covers
+    // whole row segments (16 lanes x 16 bytes of one fp32 row, 128 or 64
+    // contiguous bytes of bf16) instead of 16 bytes in each of 32 rows.  A
+    // wave's LDS accesses execute in order, so the second half may overwrite
+    // the region right after the first half's reads.
+    static_assert(WN == 64 && TM % 2 == 0, "epilogue staging shape");
+    constexpr int PR = WM / 2;                 // rows per pass
+    Q3L_LDS char* reg = lds + wave * EREG;
+    const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+    stage_barrier();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int ii = 0; ii < TM / 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& c = acc[pass * (TM / 2) + ii][j];
+            *reinterpret_cast<Q3L_LDS f32x4_t*>(
+                reg + (ii * 32 + (lane & 31)) * ERS + (j * 32 + 8 * q + hl) * 4) =
+                f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+          }
+      const int mp = mw + pass * PR;
+      if constexpr (EPI == EPI_SILU_MUL) {
+        // Staged row: g in columns 0..31, u in 32..63 (the paired operand
+        // interleaves 32-column blocks); f column = nw / 2 + c.
+#pragma unroll
+        for (int t = 0; t < PR / 8; ++t) {
+          const int row = 8 * t + (lane >> 3), c = 4 * (lane & 7);
+          const f32x4_t gv = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * c);
+          const f32x4_t uv =
+              *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 128 + 4 * c);
+          const int m = mp + row, f = nw / 2 + c;
+          if (m >= g.M || f >= e.ffn) continue;
+          float fv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) fv[r] = silu_f(gv[r]) * uv[r];
+          st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + f,
+              u32x2_t{pack2(fv[0], fv[1]), pack2(fv[2], fv[3])});
+          if (e.gu) {
+            bf16_t* G = static_cast<bf16_t*>(e.gu) + (int64_t)m * e.ldgu + f;
+            st8(G, u32x2_t{pack2(gv[0], gv[1]), pack2(gv[2], gv[3])});
+            st8(G + e.ffn, u32x2_t{pack2(uv[0], uv[1]), pack2(uv[2], uv[3])});
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < PR / 4; ++t) {
+          const int row = 4 * t + (lane >> 4), c = 4 * (lane & 15);
+          f32x4_t v = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * c);
+          const int m = mp + row, n = nw + c;
+          if (m >= g.M || n >= g.N) continue;
           if constexpr (EPI == EPI_STORE) {
             if (e.r) {
-              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) +
-                                     (int64_t)m * e.ldr + n);
+              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n);
               v[0] += lo_f(rr[0]); v[1] += hi_f(rr[0]);
               v[2] += lo_f(rr[1]); v[3] += hi_f(rr[1]);
             }
             st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n,
                 u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
           } else if constexpr (EPI == EPI_PARTIAL) {
-            *reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + n) =
-                f32x4_t{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + n) = v;
             if (e.c) {
-              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) +
-                                     (int64_t)m * e.ldr + n);
+              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n);
               st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n,
                   u32x2_t{pack2(v[0] + lo_f(rr[0]), v[1] + hi_f(rr[0])),
                           pack2(v[2] + lo_f(rr[1]), v[3] + hi_f(rr[1]))});
             }
-          } else if constexpr (EPI == EPI_SILU_BWD) {
-            const bf16_t* G = static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n;
-            const u32x2_t g2 = ld8(G), u2 = ld8(G + e.ffn);
-            const float gg[4] = {lo_f(g2[0]), hi_f(g2[0]), lo_f(g2[1]), hi_f(g2[1])};
-            const float uu[4] = {lo_f(u2[0]), hi_f(u2[0]), lo_f(u2[1]), hi_f(u2[1])};
-            float dg[4], du[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float sg = sigmoid_f(gg[r]);
-              dg[r] = v[r] * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
-              du[r] = v[r] * gg[r] * sg;
-            }
-            bf16_t* D = static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n;
-            st8(D, u32x2_t{pack2(dg[0], dg[1]), pack2(dg[2], dg[3])});
-            st8(D + e.ffn, u32x2_t{pack2(du[0], du[1]), pack2(du[2], du[3])});
           } else if constexpr (EPI == EPI_WGRAD) {
             const bool s1 = e.cnseg > 1 && m >= e.cstart[1];
             const bool s2 = e.cnseg > 2 && m >= e.cstart[2];
             float* cb = s2 ? e.cs[2] : (s1 ? e.cs[1] : e.cs[0]);
             const int cst = s2 ? e.cstart[2] : (s1 ? e.cstart[1] : e.cstart[0]);
             f32x4_t* C = reinterpret_cast<f32x4_t*>(cb + (int64_t)(m - cst) * e.ldc + n);
-            f32x4_t nv{v[0], v[1], v[2], v[3]};
-            if (e.accumulate) nv += *C;
-            *C = nv;
+            if (e.accumulate) v += *C;
+            *C = v;
           }
         }
       }
