@@ -186,7 +186,8 @@ int q3l_version(void);
 
 /* RMSNorm over rows (walkthrough page, Step 1 formula):
  *   y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w,  rstd[r] = that
- *   reciprocal (fp32).  x, y: [rows, n] dtype; w: [n] dtype. */
+ *   reciprocal (fp32).  x, y: [rows, n] dtype; w: [n] dtype; n a multiple
+ *   of 8 and at most 8192 (Q3L_EUNSUPPORTED beyond). */
 q3l_status q3l_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t n,
                            const void *x, const void *w, float eps, void *y,
                            float *rstd, void *stream);

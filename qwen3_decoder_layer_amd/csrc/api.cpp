@@ -642,6 +642,7 @@ q3l_status q3l_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t n, const void* x
                            void* stream) {
   if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
   if (rows < 0 || n <= 0 || n % 8 != 0) return fail(Q3L_EINVAL, "n must be a positive multiple of 8");
+  if (n > 8192) return fail(Q3L_EUNSUPPORTED, "n=%d exceeds 8192", n);
   Q3L_CHECK_PTR(x, "x"); Q3L_CHECK_PTR(w, "w"); Q3L_CHECK_PTR(y, "y"); Q3L_CHECK_PTR(rstd, "rstd");
   Q3L_HIP(rmsnorm_fwd(dtype, rows, n, x, w, eps, y, rstd, static_cast<hipStream_t>(stream)));
   return Q3L_OK;

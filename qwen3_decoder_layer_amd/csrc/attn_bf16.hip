@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   constexpr int NDT = DH / 32;   // 32-row tiles of d
   constexpr int RB = 2 * DH, CPR = RB / 16;
   constexpr int TB = KT * RB;    // one K or V tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // 2 stages of K, V
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // 2 K slots, 2 V slots
   Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,11 +166,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = ld16(qp + 16 * kk);
   }
 
-  // K and V tiles by direct loads; V^T operands by transposing reads.
-  auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
-  auto load_tile = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave, lane);
-    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave, lane);
+  // K and V tiles by direct loads; V^T operands by transposing reads.  The
+  // loop is software-pipelined: iteration t computes the scores of tile
+  // t+1 while it finishes tile t (softmax, then P V), so the matrix cores
+  // have independent work during the exponentials.  K and V therefore have
+  // their own two slots each with shifted lifetimes: iteration t reads
+  // K(t+1) and V(t), and starts loading K(t+2) and V(t+1) into the slots
+  // that K(t) and V(t-1) left (both drained before the previous barrier).
+  auto kslot = [&](int s) { return lds + s * TB; };
+  auto vslot = [&](int s) { return lds + (2 + s) * TB; };
+  auto load_k = [&](int t, int s) {
+    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, kslot(s), wave, lane);
+  };
+  auto load_v = [&](int t, int s) {
+    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, vslot(s), wave, lane);
   };
   uint32_t offk[NKK];
   {
@@ -181,6 +190,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   const uint32_t rowk = (uint32_t)l32 * RB;
   TrOffsets<DH> tro;
   tro.init(lane);
+  // S^T of one tile (lane: one query, 2 x 16 keys).
+  auto scores = [&](const Q3L_LDS char* sK, f32x16_t (&sc)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[c][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sc[c] = mfma32(ld_lds16(sK + rowk + 32u * RB * c + offk[kk]), qf[kk], sc[c]);
+    }
+  };
 
   f32x16_t oacc[NDT];
 #pragma unroll
@@ -190,40 +210,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   float m_run = -INFINITY, l_run = 0.f;
   const int qrow = qw0 + l32;
 
-  load_tile(0, 0);
+  load_k(0, 0);
+  if (ntiles > 1) load_k(1, 1);
+  load_v(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
-  // One K/V tile; the stage index is a compile-time constant (the loop runs
-  // two tiles per trip), so LDS addresses are a per-lane register plus an
-  // immediate offset and need no per-tile arithmetic.
-  auto tile = [&](int t, auto stage_c) {
-    constexpr int s = decltype(stage_c)::value;
-    if (t + 1 < ntiles) load_tile(t + 1, s ^ 1);
+  f32x16_t sc[2][2];          // scores of tiles t (slot t % 2) and t+1
+  scores(kslot(0), sc[0]);
+  // Iteration t; the slot parity is a compile-time constant (two iterations
+  // per trip), so LDS addresses are a per-lane register plus an immediate.
+  auto iter = [&](int t, auto par) {
+    constexpr int s = decltype(par)::value;
+    if (t + 2 < ntiles) load_k(t + 2, s);
+    if (t + 1 < ntiles) load_v(t + 1, s ^ 1);
     if (t < my_tiles) {
-      const Q3L_LDS char* sK = lds + s * 2 * TB;
-      const Q3L_LDS char* sV = sK + TB;
+      f32x16_t (&cur)[2] = sc[s];
       const int kv0 = t * KT;
-      f32x16_t sc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[c][e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          sc[c] = mfma32(ld_lds16(sK + rowk + 32u * RB * c + offk[kk]), qf[kk], sc[c]);
-      }
       const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
       float mx = -INFINITY;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float v = sc[c][e];
+          float v = cur[c][e];
           if (need_mask) {
             const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
             if (kv > qrow || kv >= L) v = -INFINITY;
           }
-          sc[c][e] = v;
+          cur[c][e] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
@@ -240,21 +254,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
       }
+      // Scores of tile t+1 (unused past this wave's last tile: the slot then
+      // holds another tile or stale data, which is harmless to read).
+      scores(kslot(s ^ 1), sc[s ^ 1]);
       const float neg = -m_run;
       float rs = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, neg));
-          sc[c][e] = pv;
+          const float pv = exp2_raw(fmaf(cur[c][e], p.scale_log2, neg));
+          cur[c][e] = pv;
           rs += pv;
         }
       rs += __shfl_xor(rs, 32, 64);
       l_run += rs;
+      const Q3L_LDS char* sV = vslot(s);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pf = pack_half(sc[ks >> 1], ks & 1);
+        const u32x4_t pf = pack_half(cur[ks >> 1], ks & 1);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(tro.read(sV, ks, dt), pf, oacc[dt]);
       }
@@ -263,8 +281,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     stage_barrier();
   };
   for (int t = 0; t < ntiles; t += 2) {
-    tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+    iter(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) iter(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (qrow >= L) return;

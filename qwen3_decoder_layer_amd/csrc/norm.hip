@@ -42,7 +42,10 @@ template <> struct V8<float> {
 };
 
 // ---- RMSNorm forward: one wave per row ------------------------------------
-template <class T>
+// The row stays in registers (CPL 8-element chunks per lane, n <= 512 CPL):
+// every load of the row is issued before the first use, so each wave has
+// the whole row in flight, and x is read once.
+template <class T, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(
     int64_t rows, int n, const T* __restrict__ x, const T* __restrict__ w,
     float eps, T* __restrict__ y, float* __restrict__ rstd) {
@@ -52,22 +55,33 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(
   const T* xr = x + row * n;
   T* yr = y + row * n;
   const int nc = n / 8;
-  float ss = 0.f;
-  for (int c = lane; c < nc; c += 64) {
-    float f[8];
-    V8<T>::load(xr + 8 * c, f);
+  float f[CPL][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nc) {
+      V8<T>::load(xr + 8 * ch, f[c]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[c][j] = 0.f;
+    }
   }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += f[c][j] * f[c][j];
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int c = lane; c < nc; c += 64) {
-    float f[8], g[8];
-    V8<T>::load(xr + 8 * c, f);
-    V8<T>::load(w + 8 * c, g);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = f[j] * r * g[j];
-    V8<T>::store(yr + 8 * c, f);
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch >= nc) continue;
+    float g[8];
+    V8<T>::load(w + 8 * ch, g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[c][j] = f[c][j] * r * g[j];
+    V8<T>::store(yr + 8 * ch, f[c]);
   }
   if (lane == 0) rstd[row] = r;
 }
@@ -528,12 +542,24 @@ hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
-  if (dtype == 1)
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16_t>, grid, block, 0, s, rows, n,
-                       (const bf16_t*)x, (const bf16_t*)w, eps, (bf16_t*)y, rstd);
-  else
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, grid, block, 0, s, rows, n,
-                       (const float*)x, (const float*)w, eps, (float*)y, rstd);
+  const int cpl = (int)cdiv(n, 512);
+#define Q3L_RF(T, C)                                                                \
+  hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, C>), grid, block, 0, s, rows, n,         \
+                     (const T*)x, (const T*)w, eps, (T*)y, rstd)
+#define Q3L_RF_ALL(T)                        \
+  if (cpl <= 1) Q3L_RF(T, 1);                \
+  else if (cpl <= 2) Q3L_RF(T, 2);           \
+  else if (cpl <= 4) Q3L_RF(T, 4);           \
+  else if (cpl <= 8) Q3L_RF(T, 8);           \
+  else if (cpl <= 16) Q3L_RF(T, 16);         \
+  else return hipErrorInvalidValue;
+  if (dtype == 1) {
+    Q3L_RF_ALL(bf16_t)
+  } else {
+    Q3L_RF_ALL(float)
+  }
+#undef Q3L_RF_ALL
+#undef Q3L_RF
   return hipGetLastError();
 }
 

@@ -187,6 +187,13 @@ def test_phase_entry_points_validate(abi, lib):
     st = lib.q3l_attention_fwd(abi.Q3L_BF16, 1, 16, 4, 2, 80, None, 0, None, 0,
                                None, 0, None, 0, None, None)
     assert st == 2
+    # A row wider than the register-resident norm kernels hold.
+    st = lib.q3l_rmsnorm_fwd(abi.Q3L_BF16, 4, 8200, None, None, 1e-6, None, None,
+                             None)
+    assert st == 2 and "8192" in err(lib)
+    st = lib.q3l_rmsnorm_fwd(abi.Q3L_BF16, 4, 12, None, None, 1e-6, None, None,
+                             None)
+    assert st == 1
 
 
 def test_version_and_missing_library_fails_loudly(abi, lib, monkeypatch):
