@@ -226,20 +226,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     if (t < my_tiles) {
       f32x16_t (&cur)[2] = sc[s];
       const int kv0 = t * KT;
-      const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
+      // Row maximum; only tiles that reach the diagonal or the sequence end
+      // mask.  The two cases are separate straight-line code paths.
       float mx = -INFINITY;
+      auto row_max = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = cur[c][e];
-          if (need_mask) {
-            const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (kv > qrow || kv >= L) v = -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            float v = cur[c][e];
+            if constexpr (decltype(masked)::value) {
+              const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
+              v = (kv > qrow || kv >= L) ? -INFINITY : v;
+              cur[c][e] = v;
+            }
+            mx = fmaxf(mx, v);
           }
-          cur[c][e] = v;
-          mx = fmaxf(mx, v);
-        }
+      };
+      if ((kv0 + KT - 1 > qw0) || (kv0 + KT > L))
+        row_max(std::true_type{});
+      else
+        row_max(std::false_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
       // The reference maximum m_run moves (and O, l are rescaled) only when a
       // row's maximum exceeds it by more than kTau: exponents stay <= kTau,

@@ -261,10 +261,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int ABYTES = BM * KB * 2, BBYTES = BN * KB * 2;
   constexpr int STAGE = ABYTES + BBYTES;
-  // The epilogue reuses the LDS: per wave, half its rows of fp32 results
-  // (rows padded by 16 bytes).
+  // The epilogue reuses the LDS: per wave, the fp32 results of one pass
+  // (rows padded by 16 bytes).  A wave's rows are staged in two passes, or
+  // one 32-row block per pass when it holds an odd number of blocks.
   constexpr int ERS = (BN / (NW / 2)) * 4 + 16;      // staged row, bytes
-  constexpr int EREG = (BM / 4) * ERS;                // per wave
+  constexpr int EPASS = (BM / 64) % 2 == 0 ? 2 : BM / 64;
+  constexpr int EREG = (BM / 2 / EPASS) * ERS;        // per wave
   constexpr int SMEM = NS * STAGE > NW * EREG ? NS * STAGE : NW * EREG;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Q3L_LDS char* lds = (Q3L_LDS char*)smem;
@@ -454,22 +456,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     // region and reads it back row-major, so every global access covers
     // whole row segments (16 lanes x 16 bytes of one fp32 row, 128 or 64
     // contiguous bytes of bf16) instead of 16 bytes in each of 32 rows.  A
-    // wave's LDS accesses execute in order, so the second half may overwrite
-    // the region right after the first half's reads.
-    static_assert(WN == 64 && TM % 2 == 0, "epilogue staging shape");
-    constexpr int PR = WM / 2;                 // rows per pass
+    // wave's LDS accesses execute in order, so a pass may overwrite the
+    // region right after the previous pass's reads.
+    static_assert(WN == 64 && TM % EPASS == 0, "epilogue staging shape");
+    constexpr int BPP = TM / EPASS;            // 32-row blocks per pass
+    constexpr int PR = 32 * BPP;               // rows per pass
     Q3L_LDS char* reg = lds + wave * EREG;
     const int mw = m0 + wm * WM, nw = n0 + wn * WN;
     stage_barrier();
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < EPASS; ++pass) {
 #pragma unroll
-      for (int ii = 0; ii < TM / 2; ++ii)
+      for (int ii = 0; ii < BPP; ++ii)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x16_t& c = acc[pass * (TM / 2) + ii][j];
+            const f32x16_t& c = acc[pass * BPP + ii][j];
             *reinterpret_cast<Q3L_LDS f32x4_t*>(
                 reg + (ii * 32 + (lane & 31)) * ERS + (j * 32 + 8 * q + hl) * 4) =
                 f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
@@ -571,7 +574,19 @@ hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s) {
   auto tiles = [&](int bm, int bn) {
     return (int64_t)((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= kCUs) return launch_layout<256, 256, 64, 2, 8>(g, s);
+  auto rounds = [&](int64_t t) { return (t + kCUs - 1) / kCUs; };
+  if (tiles(256, 256) >= kCUs) {
+    // Tiles go to the CUs in rounds, and a ragged last round costs a whole
+    // one.  A round of 192 x 256 tiles takes about 0.92 of a round of
+    // 256 x 256 tiles (measured at 6144 x 4096 x 8192), so the shorter tile
+    // wins where it needs as few rounds (there: 2 rounds of 512 tiles
+    // against 1.5 of 384).  K-contiguous operands only: the row-contiguous
+    // loader assumes a power-of-two tile height.
+    if (g.a.k_contig && g.b.k_contig &&
+        23 * rounds(tiles(192, 256)) < 25 * rounds(tiles(256, 256)))
+      return launch_epi<192, 256, 64, 2, 8, true, true>(g, s);
+    return launch_layout<256, 256, 64, 2, 8>(g, s);
+  }
   if (tiles(256, 128) >= kCUs) return launch_layout<256, 128, 64, 2, 4>(g, s);
   return launch_layout<128, 128, 64, 2, 4>(g, s);
 }
