@@ -431,23 +431,29 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
       }
       // lane: key mykv; rows q = qh0 + 8(e/4) + 4h + e%4 -- four consecutive
       // rows per e/4, so LSE and delta come in float4s.
-      const bool need_mask = (qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L);
+      // P in place of S, then dS = P (dP - D); only blocks that reach the
+      // diagonal or the sequence end mask, in a loop of their own.
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int qb = 32 * half + 8 * e4 + 4 * h;
         const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qb]) * kLog2e;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sc[4 * e4 + r] = exp2_raw(fmaf(sc[4 * e4 + r], p.scale_log2, -lq[r]));
+      }
+      if ((qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int q = qh0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          sc[e] = (mykv > q || q >= L || mykv >= L) ? 0.f : sc[e];
+        }
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int qb = 32 * half + 8 * e4 + 4 * h;
         const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qb]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * e4 + r;
-          float pv = exp2_raw(fmaf(sc[e], p.scale_log2, -lq[r]));
-          if (need_mask) {
-            const int q = qh0 + 8 * e4 + 4 * h + r;
-            if (mykv > q || q >= L || mykv >= L) pv = 0.f;
-          }
-          sc[e] = pv;
-          dp[e] = pv * (dp[e] - dq4[r]);
-        }
+        for (int r = 0; r < 4; ++r) dp[4 * e4 + r] = sc[4 * e4 + r] * (dp[4 * e4 + r] - dq4[r]);
       }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
@@ -593,18 +599,25 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
           dp[c] = mfma32(ld_lds16(sV + o), of[kk], dp[c]);
         }
       }
-      const bool need_mask = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
+      // P in place of S; only tiles that reach the diagonal or the sequence
+      // end mask, in a loop of their own after the exponentials.
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = exp2_raw(fmaf(sc[c][e], p.scale_log2, -lse2));
-          if (need_mask) {
+        for (int e = 0; e < 16; ++e) sc[c][e] = exp2_raw(fmaf(sc[c][e], p.scale_log2, -lse2));
+      if ((kv0 + KT - 1 > qw0) || (kv0 + KT > L)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
             const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (kv > qrow || kv >= L) pv = 0.f;
+            sc[c][e] = (kv > qrow || kv >= L) ? 0.f : sc[c][e];
           }
-          dp[c][e] = pv * (dp[c][e] - dlt);
-        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[c][e] = sc[c][e] * (dp[c][e] - dlt);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);

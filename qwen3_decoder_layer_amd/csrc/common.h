@@ -102,6 +102,7 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
 
 // ---- LDS: direct loads from global memory and transposing reads ----------
 #define Q3L_LDS __attribute__((address_space(3)))
+#define Q3L_GLOBAL __attribute__((address_space(1)))
 
 __device__ inline uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline uint64_t uni64(uint64_t v) {

@@ -452,8 +452,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     }
   } else {
     // Staged through LDS: once every wave is past its last fragment read,
-    // each wave writes half of its fp32 sub-tile at a time into its own LDS
-    // region and reads it back row-major, so every global access covers
+    // each wave writes its fp32 sub-tile one pass (half, or a third) at a
+    // time into its own LDS region and reads it back row-major, so every global access covers
     // whole row segments (16 lanes x 16 bytes of one fp32 row, 128 or 64
     // contiguous bytes of bf16) instead of 16 bytes in each of 32 rows.  A
     // wave's LDS accesses execute in order, so a pass may overwrite the
@@ -461,11 +461,43 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     static_assert(WN == 64 && TM % EPASS == 0, "epilogue staging shape");
     constexpr int BPP = TM / EPASS;            // 32-row blocks per pass
     constexpr int PR = 32 * BPP;               // rows per pass
+    constexpr int NT = PR / 4;                 // row groups per pass (plain epilogues)
     Q3L_LDS char* reg = lds + wave * EREG;
     const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+    // Plain epilogues: in pass p, lane reads staged row 4t + lane/16 (t <
+    // NT), columns 4 (lane % 16) .. +3.  The bf16 residual they add is
+    // requested for every pass before the first barrier, at addresses
+    // clamped into the matrix where the tile overhangs it, so the loads
+    // overlap one another and the staging instead of each waiting in turn.
+    const int cn = 4 * (lane & 15), nn = nw + cn;
+    const int nclamp = nn < g.N ? nn : g.N - 4;
+    const bf16_t* resid = nullptr;
+    if constexpr (EPI == EPI_STORE) resid = static_cast<const bf16_t*>(e.r);
+    if constexpr (EPI == EPI_PARTIAL) resid = e.c ? static_cast<const bf16_t*>(e.r) : nullptr;
+    u32x2_t rr[EPASS][NT];
+    // Weight-gradient output segments, read once into registers: selecting
+    // among fields of the argument block per lane would make the compiler
+    // load them from memory for every row.
+    const int wg_nseg = (int)uni((uint32_t)e.cnseg);
+    const int wg_st1 = (int)uni((uint32_t)e.cstart[1]), wg_st2 = (int)uni((uint32_t)e.cstart[2]);
+    const uint64_t wg_c0 = uni64((uint64_t)e.cs[0]), wg_c1 = uni64((uint64_t)e.cs[1]),
+                   wg_c2 = uni64((uint64_t)e.cs[2]);
+    if constexpr (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
+      if (resid) {
+#pragma unroll
+        for (int pass = 0; pass < EPASS; ++pass)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            int m = mw + pass * PR + 4 * t + (lane >> 4);
+            if (m > g.M - 1) m = g.M - 1;
+            rr[pass][t] = ld8(resid + (int64_t)m * e.ldr + nclamp);
+          }
+      }
+    }
     stage_barrier();
 #pragma unroll
     for (int pass = 0; pass < EPASS; ++pass) {
+      const int mp = mw + pass * PR;
 #pragma unroll
       for (int ii = 0; ii < BPP; ++ii)
 #pragma unroll
@@ -477,7 +509,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
                 reg + (ii * 32 + (lane & 31)) * ERS + (j * 32 + 8 * q + hl) * 4) =
                 f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
           }
-      const int mp = mw + pass * PR;
       if constexpr (EPI == EPI_SILU_MUL) {
         // Staged row: g in columns 0..31, u in 32..63 (the paired operand
         // interleaves 32-column blocks); f column = nw / 2 + c.
@@ -502,33 +533,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < PR / 4; ++t) {
-          const int row = 4 * t + (lane >> 4), c = 4 * (lane & 15);
-          f32x4_t v = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * c);
-          const int m = mp + row, n = nw + c;
-          if (m >= g.M || n >= g.N) continue;
+        for (int t = 0; t < NT; ++t) {
+          const int row = 4 * t + (lane >> 4);
+          f32x4_t v = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * cn);
+          const int m = mp + row;
+          if (m >= g.M || nn >= g.N) continue;
           if constexpr (EPI == EPI_STORE) {
-            if (e.r) {
-              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n);
-              v[0] += lo_f(rr[0]); v[1] += hi_f(rr[0]);
-              v[2] += lo_f(rr[1]); v[3] += hi_f(rr[1]);
+            if (resid) {
+              v[0] += lo_f(rr[pass][t][0]); v[1] += hi_f(rr[pass][t][0]);
+              v[2] += lo_f(rr[pass][t][1]); v[3] += hi_f(rr[pass][t][1]);
             }
-            st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n,
+            st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
                 u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
           } else if constexpr (EPI == EPI_PARTIAL) {
-            *reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + n) = v;
-            if (e.c) {
-              const u32x2_t rr = ld8(static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n);
-              st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + n,
-                  u32x2_t{pack2(v[0] + lo_f(rr[0]), v[1] + hi_f(rr[0])),
-                          pack2(v[2] + lo_f(rr[1]), v[3] + hi_f(rr[1]))});
+            *reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + nn) = v;
+            if (resid) {
+              const u32x2_t r2 = rr[pass][t];
+              st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
+                  u32x2_t{pack2(v[0] + lo_f(r2[0]), v[1] + hi_f(r2[0])),
+                          pack2(v[2] + lo_f(r2[1]), v[3] + hi_f(r2[1]))});
             }
           } else if constexpr (EPI == EPI_WGRAD) {
-            const bool s1 = e.cnseg > 1 && m >= e.cstart[1];
-            const bool s2 = e.cnseg > 2 && m >= e.cstart[2];
-            float* cb = s2 ? e.cs[2] : (s1 ? e.cs[1] : e.cs[0]);
-            const int cst = s2 ? e.cstart[2] : (s1 ? e.cstart[1] : e.cstart[0]);
-            f32x4_t* C = reinterpret_cast<f32x4_t*>(cb + (int64_t)(m - cst) * e.ldc + n);
+            const bool s1 = wg_nseg > 1 && m >= wg_st1;
+            const bool s2 = wg_nseg > 2 && m >= wg_st2;
+            const uint64_t cb = s2 ? wg_c2 : (s1 ? wg_c1 : wg_c0);
+            const int cst = s2 ? wg_st2 : (s1 ? wg_st1 : 0);
+            Q3L_GLOBAL f32x4_t* C = reinterpret_cast<Q3L_GLOBAL f32x4_t*>(
+                cb + ((uint64_t)(m - cst) * e.ldc + nn) * 4);
             if (e.accumulate) v += *C;
             *C = v;
           }
