@@ -66,14 +66,22 @@ __device__ inline float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS row layout of the K/V/Q/dO tiles: a [rows][d_h] bf16 tile
 // stored row-major with its 16-byte chunks permuted per row: chunk c of row
-// r sits at slot c ^ swz(r).  swz is a bijection on the low bits of r, so
-// the 16-byte reads of 16 consecutive rows at one chunk hit distinct banks,
-// and it moves the chunk PAIR {2m, 2m+1} as a unit with distinct pairs for
-// any 4 aligned consecutive rows, so the transposing 8-byte reads (4 rows x
-// 32 contiguous bytes per 16-lane group) are conflict-free as well.
+// r sits at slot c ^ swz(r).  The LDS serves 256 bytes (64 banks of 4) per
+// cycle: 16 lanes of a 16-byte read, 32 lanes of an 8-byte read.  swz(r)
+// depends on r mod 16 only and is chosen so that both read patterns find
+// 256 distinct bytes in every cycle:
+//  - 16-byte reads of 16 aligned consecutive rows at one chunk: swz is a
+//    bijection on each aligned block of 16 rows (two 128-byte rows share
+//    a bank line when d_h = 64, so there the even and the odd rows each
+//    need distinct slots);
+//  - transposing 8-byte reads, 32 lanes = 4 aligned rows x 4 consecutive
+//    chunks (an aligned quad): the quads c ^ swz(r) of the 4 rows (of the
+//    2 rows that share bank lines, at d_h = 64) are distinct, i.e. swz(r) / 4
+//    differs between them.
 template <int CPR>
 __device__ inline int swz(int r) {
-  return ((r & (CPR / 2 - 1)) << 1) | ((r / (CPR / 2)) & 1);
+  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Rows r0 .. r0+NR-1 (token positions of one sequence starting at token
