@@ -115,7 +115,7 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    k_ms = time_dominant(lc, W["gate"], W["up"], stream, max(10, steps))
+    k_ms = time_dominant(lc, W["gate"], W["up"], stream, max(10, steps), between=step)
     del saved
     return {"elapsed": elapsed, "kernel_ms": k_ms}
 
@@ -130,22 +130,29 @@ def dominant_operands(lc, gate, up):
     return hn, f, gu
 
 
-def time_dominant(lc, gate, up, stream, reps: int) -> float:
+def time_dominant(lc, gate, up, stream, reps: int, between=None) -> float:
     """Average duration (ms) of the fused gate/up GEMM + SwiGLU kernel at the
-    layer's shapes, with HIP events recorded on the stream it launches on."""
+    layer's shapes, with HIP events recorded on the stream it launches on.
+
+    With `between` (one layer step), each timed launch follows a step, so
+    the kernel runs under the same clock and cache conditions as inside the
+    timed steps; launched back to back instead, the sustained matrix-core
+    load lowers the clock and the kernel runs a few per cent slower."""
     import torch
     import qwen3_decoder_layer_amd as q3
     hn, f, gu = dominant_operands(lc, gate, up)
     for _ in range(3):
         q3.swiglu_fwd(hn, gate, up, f=f, gu=gu, stream=stream)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(reps):
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+    for ev0, ev1 in pairs:
+        if between is not None:
+            between()
+        ev0.record(stream)
         q3.swiglu_fwd(hn, gate, up, f=f, gu=gu, stream=stream)
-    ev1.record(stream)
+        ev1.record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / reps
+    return sum(a.elapsed_time(b) for a, b in pairs) / reps
 
 
 def dominant_work(T: int, d: int, f: int) -> tuple:

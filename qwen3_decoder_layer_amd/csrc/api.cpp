@@ -473,17 +473,17 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   char* tA = bt ? at(workspace, W.tA) : nullptr;
   char* tB = bt ? at(workspace, W.tB) : nullptr;
   char* tC = bt ? at(workspace, W.tC) : nullptr;
-  if (bt) {
-    Q3L_HIP(transpose_bf16(m.d, m.d, m.ffn, w->down, m.ffn, wt_down, m.d, s));
-    Q3L_HIP(transpose_bf16(m.ffn, m.ffn, m.d, w->gate, m.d, wt_gu, 2 * m.ffn, s));
-    Q3L_HIP(transpose_bf16(m.ffn, m.ffn, m.d, w->up, m.d, wt_gu + (size_t)m.ffn * 2,
-                           2 * m.ffn, s));
-    Q3L_HIP(transpose_bf16(m.d, m.d, m.qd, w->o, m.qd, wt_o, m.d, s));
-    Q3L_HIP(transpose_bf16(m.qd, m.qd, m.d, w->q, m.d, wt_qkv, m.nqkv, s));
-    Q3L_HIP(transpose_bf16(m.kvd, m.kvd, m.d, w->k, m.d, wt_qkv + (size_t)m.qd * 2,
-                           m.nqkv, s));
-    Q3L_HIP(transpose_bf16(m.kvd, m.kvd, m.d, w->v, m.d,
-                           wt_qkv + (size_t)(m.qd + m.kvd) * 2, m.nqkv, s));
+  if (bt) {   // the seven weight transposes, one launch
+    const int d = m.d, ffn = m.ffn, qd = m.qd, kvd = m.kvd;
+    const TransposeJob jobs[7] = {
+        {w->down, ffn, wt_down, d, d, d, ffn},
+        {w->gate, d, wt_gu, 2 * (int64_t)ffn, ffn, ffn, d},
+        {w->up, d, wt_gu + (size_t)ffn * 2, 2 * (int64_t)ffn, ffn, ffn, d},
+        {w->o, qd, wt_o, d, d, d, qd},
+        {w->q, d, wt_qkv, m.nqkv, qd, qd, d},
+        {w->k, d, wt_qkv + (size_t)qd * 2, m.nqkv, kvd, kvd, d},
+        {w->v, d, wt_qkv + (size_t)(qd + kvd) * 2, m.nqkv, kvd, kvd, d}};
+    Q3L_HIP(transpose_bf16_batch(jobs, 7, s));
   }
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
   // feature counts; A/B activations with row strides lda/ldb).  bf16: A and
@@ -496,9 +496,11 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     if (bt) {
       char* ta = tA_ ? tA_ : tA;
       char* tb = tB_ ? tB_ : tB;
-      hipError_t err = a_done ? hipSuccess : transpose_bf16(T, Tp, ma, A, lda, ta, Tp, s);
-      if (err != hipSuccess) return err;
-      err = b_done ? hipSuccess : transpose_bf16(T, Tp, nb, B, ldb, tb, Tp, s);
+      TransposeJob jobs[2];
+      int nj = 0;
+      if (!a_done) jobs[nj++] = TransposeJob{A, lda, ta, Tp, T, Tp, ma};
+      if (!b_done) jobs[nj++] = TransposeJob{B, ldb, tb, Tp, T, Tp, nb};
+      const hipError_t err = transpose_bf16_batch(jobs, nj, s);   // one launch
       if (err != hipSuccess) return err;
       g.a = kop(ta, Tp, ma);
       g.b = kop(tb, Tp, nb);

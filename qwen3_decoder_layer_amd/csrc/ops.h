@@ -70,6 +70,15 @@ hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
 // [rows, rows_pad) are zero.  rows_pad and cols multiples of 8.
 hipError_t transpose_bf16(int rows, int rows_pad, int cols, const void* src,
                           int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s);
+// Up to kTransposeBatchMax transposes in one launch (jobs with no work are
+// skipped).
+constexpr int kTransposeBatchMax = 8;
+struct TransposeJob {
+  const void* src; int64_t ld_src;
+  void* dst; int64_t ld_dst;
+  int rows, rows_pad, cols;
+};
+hipError_t transpose_bf16_batch(const TransposeJob* jobs, int n, hipStream_t s);
 
 // SwiGLU adjoint, bf16: from df [T, ffn] and the saved g|u [T, 2 ffn] write
 // dgu = [dg | du] ([T, 2 ffn]) and, if dguT is not null, its transpose dguT
