@@ -223,7 +223,10 @@ q3l_status q3l_swiglu_fwd(int32_t dtype, int64_t M, int32_t N, int32_t K,
 /* Causal GQA attention (walkthrough page, Step 5) on one batch:
  *   q [B*L, h_q*d_h] with row stride ldq, k/v [B*L, h_kv*d_h] with row
  *   strides ldk/ldv, o [B*L, h_q*d_h] with row stride ldo (dtype);
- *   lse [B, h_q, L] fp32 (natural log).  Scale 1/sqrt(d_h). */
+ *   lse [B, h_q, L] fp32 (natural log).  Scale 1/sqrt(d_h).
+ *   bf16: (B*L + 64) * max(ldq, ldk, ldv, ldo) * 2 and B*L*h_q*4 must stay
+ *   below 2^31 (Q3L_EUNSUPPORTED otherwise; the same bound holds for
+ *   q3l_attention_bwd). */
 q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L,
                              int32_t h_q, int32_t h_kv, int32_t d_h,
                              const void *q, int64_t ldq, const void *k,

@@ -725,6 +725,19 @@ static q3l_status check_attn(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   return Q3L_OK;
 }
 
+// The bf16 attention kernels stage Q/K/V/dO tiles and the per-query
+// statistics with 32-bit byte offsets from each tensor's base.
+static q3l_status check_attn_range(int32_t dtype, int32_t B, int32_t L, int32_t h_q,
+                                   int64_t ld_max) {
+  if (dtype != Q3L_BF16) return Q3L_OK;
+  const int64_t T = (int64_t)B * L;
+  if ((T + 64) * ld_max * 2 >= (1LL << 31) || T * h_q * 4 >= (1LL << 31))
+    return fail(Q3L_EUNSUPPORTED, "B*L=%lld tokens with row stride %lld exceeds the 2 GiB "
+                "offset range of the bf16 attention kernels", (long long)T,
+                (long long)ld_max);
+  return Q3L_OK;
+}
+
 q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
                              int32_t d_h, const void* q, int64_t ldq, const void* k,
                              int64_t ldk, const void* v, int64_t ldv, void* o, int64_t ldo,
@@ -736,6 +749,9 @@ q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   if (ldq < (int64_t)h_q * d_h || ldk < (int64_t)h_kv * d_h || ldv < (int64_t)h_kv * d_h ||
       ldo < (int64_t)h_q * d_h || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
     return fail(Q3L_EINVAL, "row strides too small or not multiples of 8");
+  if ((st = check_attn_range(dtype, B, L, h_q,
+                             std::max(std::max(ldq, ldk), std::max(ldv, ldo)))) != Q3L_OK)
+    return st;
   AttnArgs a{};
   a.B = B; a.L = L; a.h_q = h_q; a.h_kv = h_kv; a.d_h = d_h;
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv;
@@ -766,6 +782,9 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   if (ldq < (int64_t)h_q * d_h || ldk < (int64_t)h_kv * d_h || ldv < (int64_t)h_kv * d_h ||
       ldo < (int64_t)h_q * d_h || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
     return fail(Q3L_EINVAL, "row strides too small or not multiples of 8");
+  if ((st = check_attn_range(dtype, B, L, h_q,
+                             std::max(std::max(ldq, ldk), std::max(ldv, ldo)))) != Q3L_OK)
+    return st;
   AttnArgs a{};
   a.B = B; a.L = L; a.h_q = h_q; a.h_kv = h_kv; a.d_h = d_h;
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv;

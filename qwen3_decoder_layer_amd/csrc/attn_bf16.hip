@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   stage_barrier();
   f32x16_t sc[2][2];          // scores of tiles t (slot t % 2) and t+1
   scores(kslot(0), sc[0]);
+  stage_barrier();            // K(0) read by every wave before its slot is refilled
   // Iteration t; the slot parity is a compile-time constant (two iterations
   // per trip), so LDS addresses are a per-lane register plus an immediate.
   auto iter = [&](int t, auto par) {

@@ -196,6 +196,23 @@ def test_phase_entry_points_validate(abi, lib):
     assert st == 1
 
 
+def test_attention_offset_range_is_checked(abi, lib):
+    # Valid-looking (aligned, non-null) host addresses: the call must reject
+    # the sizes before any launch, since a 1M-token bf16 batch with 4096-wide
+    # rows overruns the kernels' 32-bit byte offsets.
+    buf = C.create_string_buffer(256)
+    p = C.c_void_p((C.addressof(buf) + 15) // 16 * 16)
+    L, hq, hkv, dh = 1 << 20, 32, 8, 128
+    st = lib.q3l_attention_fwd(abi.Q3L_BF16, 1, L, hq, hkv, dh, p, hq * dh, p,
+                               hkv * dh, p, hkv * dh, p, hq * dh, p, None)
+    assert st == 2 and "2 GiB" in err(lib)
+    ws = lib.q3l_attention_bwd_workspace_bytes(1, L, hq)
+    st = lib.q3l_attention_bwd(abi.Q3L_BF16, 1, L, hq, hkv, dh, p, hq * dh, p,
+                               hkv * dh, p, hkv * dh, p, p, hq * dh, p, p, p, p, p,
+                               ws, None)
+    assert st == 2 and "2 GiB" in err(lib)
+
+
 def test_version_and_missing_library_fails_loudly(abi, lib, monkeypatch):
     assert lib.q3l_version() >= 1
     # No fallback: without the built library the binding raises.
