@@ -174,13 +174,15 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
 }
 
 // bf16 form of the same: a row's dy and x chunks are loaded once, all up
-// front, and kept packed in registers across the reduction; w stays in
-// registers for every row.  Residual bf16 (resid_f32 = 0) or fp32.
-template <int CPL>
+// front, and kept packed in registers; w is read from LDS for every row.
+// The residual (RK: 0 none, 1 bf16, 2 fp32) is requested with them when it
+// is bf16 (it does not wait for the row reduction); an fp32 residual would
+// need twice the registers and is read after the reduction.
+template <int CPL, int RK>
 __global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
     int64_t rows, int n, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ x,
     const float* __restrict__ rstd, const bf16_t* __restrict__ w,
-    const void* __restrict__ resid, int resid_f32, bf16_t* __restrict__ dx,
+    const void* __restrict__ resid, bf16_t* __restrict__ dx,
     float* __restrict__ dx32, float* __restrict__ wpart) {
   extern __shared__ float sdw[];  // [n] dw partial, then w as bf16 [n]
   bf16_t* sw = reinterpret_cast<bf16_t*>(sdw + n);
@@ -201,13 +203,14 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
     // unpacked copy from being held in registers across rows).
     asm volatile("" ::: "memory");
     const float r = rstd[row];
-    u32x4_t ar[CPL], br[CPL];
+    u32x4_t ar[CPL], br[CPL], rb[RK == 1 ? CPL : 1];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nc) {
         ar[c] = ld16(dy + row * n + 8 * ch);
         br[c] = ld16(x + row * n + 8 * ch);
+        if constexpr (RK == 1) rb[c] = ld16(static_cast<const bf16_t*>(resid) + row * n + 8 * ch);
       }
     }
     float dot = 0.f;
@@ -236,16 +239,15 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
       const int ch = lane + 64 * c;
       if (ch < nc) {
         float rr[8];
-        if (resid_f32) {
+        if constexpr (RK == 2) {
           const float* rp = static_cast<const float*>(resid) + row * n + 8 * ch;
           const f32x4_t u = *reinterpret_cast<const f32x4_t*>(rp);
           const f32x4_t v = *reinterpret_cast<const f32x4_t*>(rp + 4);
 #pragma unroll
           for (int j = 0; j < 4; ++j) { rr[j] = u[j]; rr[4 + j] = v[j]; }
-        } else if (resid) {
-          const u32x4_t v = ld16(static_cast<const bf16_t*>(resid) + row * n + 8 * ch);
+        } else if constexpr (RK == 1) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { rr[2 * j] = lo_f(v[j]); rr[2 * j + 1] = hi_f(v[j]); }
+          for (int j = 0; j < 4; ++j) { rr[2 * j] = lo_f(rb[c][j]); rr[2 * j + 1] = hi_f(rb[c][j]); }
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) rr[j] = 0.f;
@@ -504,18 +506,23 @@ hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
     if (grid > kNormBwdParts) grid = kNormBwdParts;
     if (grid < 1) grid = 1;
     *nparts = (int)grid;
-#define Q3L_RB16(C)                                                                \
-  hipLaunchKernelGGL((rmsnorm_bwd_bf16_kernel<C>), dim3(grid), dim3(512),          \
+#define Q3L_RB16K(C, K)                                                            \
+  hipLaunchKernelGGL((rmsnorm_bwd_bf16_kernel<C, K>), dim3(grid), dim3(512),       \
                      shm + (size_t)n * 2, s,                                       \
                      rows, n, (const bf16_t*)dy, (const bf16_t*)x, rstd,           \
-                     (const bf16_t*)w, resid, resid_f32, (bf16_t*)dx, dx32, wpart)
-    if (cpl <= 1) Q3L_RB16(1);
-    else if (cpl <= 2) Q3L_RB16(2);
-    else if (cpl <= 4) Q3L_RB16(4);
-    else if (cpl <= 8) Q3L_RB16(8);
-    else if (cpl <= 16) Q3L_RB16(16);
+                     (const bf16_t*)w, resid, (bf16_t*)dx, dx32, wpart)
+#define Q3L_RB16(C)                              \
+  if (!resid) Q3L_RB16K(C, 0);                   \
+  else if (!resid_f32) Q3L_RB16K(C, 1);          \
+  else Q3L_RB16K(C, 2);
+    if (cpl <= 1) { Q3L_RB16(1) }
+    else if (cpl <= 2) { Q3L_RB16(2) }
+    else if (cpl <= 4) { Q3L_RB16(4) }
+    else if (cpl <= 8) { Q3L_RB16(8) }
+    else if (cpl <= 16) { Q3L_RB16(16) }
     else return hipErrorInvalidValue;
 #undef Q3L_RB16
+#undef Q3L_RB16K
     return hipGetLastError();
   }
 #define Q3L_RB(C)                                                              \
