@@ -43,8 +43,9 @@ template <> struct V8<float> {
 
 // ---- RMSNorm forward: one wave per row ------------------------------------
 // The row stays in registers (CPL 8-element chunks per lane, n <= 512 CPL):
-// every load of the row is issued before the first use, so each wave has
-// the whole row in flight, and x is read once.
+// every load of the row, and of the weight, is issued before the first use,
+// so each wave has the whole row in flight and x is read once.  bf16 rows
+// and weights stay packed (half the registers of fp32 copies).
 template <class T, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(
     int64_t rows, int n, const T* __restrict__ x, const T* __restrict__ w,
@@ -55,35 +56,67 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(
   const T* xr = x + row * n;
   T* yr = y + row * n;
   const int nc = n / 8;
-  float f[CPL][8];
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    u32x4_t xv[CPL], wv[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nc) {
-      V8<T>::load(xr + 8 * ch, f[c]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[c][j] = 0.f;
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      xv[c] = ch < nc ? ld16(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+      wv[c] = ch < nc ? ld16(w + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = lo_f(xv[c][j]), b = hi_f(xv[c][j]);
+        ss += a * a;
+        ss += b * b;
+      }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)n + eps);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch >= nc) continue;
+      u32x4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = pack2(lo_f(xv[c][j]) * r * lo_f(wv[c][j]), hi_f(xv[c][j]) * r * hi_f(wv[c][j]));
+      st16(yr + 8 * ch, o);
+    }
+    if (lane == 0) rstd[row] = r;
+  } else {
+    float f[CPL][8];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        V8<T>::load(xr + 8 * ch, f[c]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[c][j] = 0.f;
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += f[c][j] * f[c][j];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)n + eps);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch >= nc) continue;
+      float g[8];
+      V8<T>::load(w + 8 * ch, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[c][j] = f[c][j] * r * g[j];
+      V8<T>::store(yr + 8 * ch, f[c]);
+    }
+    if (lane == 0) rstd[row] = r;
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss += f[c][j] * f[c][j];
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)n + eps);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch >= nc) continue;
-    float g[8];
-    V8<T>::load(w + 8 * ch, g);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f[c][j] = f[c][j] * r * g[j];
-    V8<T>::store(yr + 8 * ch, f[c]);
-  }
-  if (lane == 0) rstd[row] = r;
 }
 
 // ---- RMSNorm backward -----------------------------------------------------
