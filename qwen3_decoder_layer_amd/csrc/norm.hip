@@ -386,8 +386,14 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
   const int hh = (int)(it % heads);
   const int pos = (int)(t % L);
   const bool isq = hh < h_q;
-  float v[8], wv[8];
+  // Every load (the vector, its norm weight, the rotation row) is issued
+  // before the first use: none waits behind the norm's reduction.
+  float v[8], wv[8], cs[8], sn[8];
   V8<T>::load(in + t * ld_in + (int64_t)hh * DH + 8 * j, v);
+  if (qk_norm) V8<T>::load((isq ? wq : wk) + 8 * j, wv);
+  const int i0 = 8 * (j % HALF);
+  V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
+  V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
   float r = 1.f;
   if (qk_norm) {
     float ss = 0.f;
@@ -395,22 +401,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     ss = group_sum(ss, LP);
     r = 1.0f / sqrtf(ss / (float)DH + eps);
-    V8<T>::load((isq ? wq : wk) + 8 * j, wv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * r * wv[e];
   }
   float pv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) pv[e] = __shfl_xor(v[e], HALF, 64);
-  const int i0 = 8 * (j % HALF);
-  const float* cr = cos_t + (int64_t)pos * (DH / 2) + i0;
-  const float* sr = sin_t + (int64_t)pos * (DH / 2) + i0;
   float o[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float c = cr[e], s = sr[e];
-    o[e] = (j < HALF) ? v[e] * c - pv[e] * s : v[e] * c + pv[e] * s;
-  }
+  for (int e = 0; e < 8; ++e)
+    o[e] = (j < HALF) ? v[e] * cs[e] - pv[e] * sn[e] : v[e] * cs[e] + pv[e] * sn[e];
   if (!valid) return;
   V8<T>::store(out + t * ld_out + (int64_t)hh * DH + 8 * j, o);
   if (qk_norm && j == 0) {
@@ -457,24 +457,26 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
     const int hh = (int)(it % heads);
     const int pos = (int)(t % L);
     const bool isq = hh < h_q;
-    float gv[8], pg[8];
+    // Every load of the item (gradient, rotation row, pre-norm vector and its
+    // rstd) is issued before the first use.
+    float gv[8], pg[8], cs[8], sn[8], xv[8];
     V8<T>::load(g + t * ld_g + (int64_t)hh * DH + 8 * j, gv);
+    const int i0 = 8 * (j % HALF);
+    V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
+    V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
+    float r = 1.f;
+    if (qk_norm) {
+      V8<T>::load(pre + t * ld_pre + (int64_t)hh * DH + 8 * j, xv);
+      r = isq ? rstd_q[t * h_q + hh] : rstd_k[t * h_kv + (hh - h_q)];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) pg[e] = __shfl_xor(gv[e], HALF, 64);
-    const int i0 = 8 * (j % HALF);
-    const float* cr = cos_t + (int64_t)pos * (DH / 2) + i0;
-    const float* sr = sin_t + (int64_t)pos * (DH / 2) + i0;
     float dn[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float c = cr[e], s = sr[e];
-      dn[e] = (j < HALF) ? gv[e] * c + pg[e] * s : gv[e] * c - pg[e] * s;
-    }
+    for (int e = 0; e < 8; ++e)
+      dn[e] = (j < HALF) ? gv[e] * cs[e] + pg[e] * sn[e] : gv[e] * cs[e] - pg[e] * sn[e];
     float o[8];
     if (qk_norm) {
-      float xv[8];
-      V8<T>::load(pre + t * ld_pre + (int64_t)hh * DH + 8 * j, xv);
-      const float r = isq ? rstd_q[t * h_q + hh] : rstd_k[t * h_kv + (hh - h_q)];
       const float* wv = isq ? wqv : wkv;
       float dot = 0.f;
 #pragma unroll
