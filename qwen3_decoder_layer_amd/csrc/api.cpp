@@ -129,7 +129,7 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
 }
 
 struct BwdWs {
-  size_t dgu, dhn, dh32, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
+  size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
   // bf16 only: transposed weights ([in, out]) and three scratch buffers for
   // the transposed operands of the weight-gradient GEMMs ([features, Tp]).
   size_t wt_down, wt_gu, wt_o, wt_qkv, tA, tB, tC;
@@ -145,7 +145,6 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
   auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
   w.dgu = take(m.T * 2 * (size_t)m.ffn * m.es);
   w.dhn = take(m.T * m.d * m.es);
-  w.dh32 = take(m.T * m.d * 4);
   w.dh = take(m.T * m.d * m.es);
   w.dO = take(m.T * m.qd * m.es);
   w.delta = take((size_t)m.B * m.hq * m.L * 4);
@@ -448,7 +447,6 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   const void* f = at(saved, L.f);
   void* dgu = at(workspace, W.dgu);
   void* dhn = at(workspace, W.dhn);
-  float* dh32 = reinterpret_cast<float*>(at(workspace, W.dh32));
   void* dh = at(workspace, W.dh);
   void* dO = at(workspace, W.dO);
   float* delta = reinterpret_cast<float*>(at(workspace, W.delta));
@@ -563,8 +561,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   // Steps 8 and 10: post-attention RMSNorm adjoint plus the residual dy.
   {
     int np = 0;
-    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dhn, h, rstd2, w->post_norm, dy, 0, dh, dh32,
-                        wpart, &np, s));
+    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dhn, h, rstd2, w->post_norm, dy, dh, wpart, &np, s));
     if (want_w) Q3L_HIP(reduce_rows(wpart, np, m.d, grads->post_norm, acc, s));
   }
   // Step 6: dO = dh W_o.
@@ -625,11 +622,11 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     e.cnseg = 3;
     Q3L_HIP(wgrad(dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e));
   }
-  // Step 1: input RMSNorm adjoint plus the attention residual (fp32 dh).
+  // Step 1: input RMSNorm adjoint plus the attention residual dh.
   {
     int np = 0;
-    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dxn, x, rstd1, w->in_norm, dh32, 1,
-                        want_dx ? dx : nullptr, nullptr, wpart, &np, s));
+    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dxn, x, rstd1, w->in_norm, dh,
+                        want_dx ? dx : nullptr, wpart, &np, s));
     if (want_w) Q3L_HIP(reduce_rows(wpart, np, m.d, grads->in_norm, acc, s));
   }
   g_err.clear();

@@ -400,16 +400,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   wait_vmcnt<0>();
   stage_barrier();
 
-  // Per-lane LDS offsets.  16-byte reads (rows 32 half + l32 of a Q/dO tile
-  // and rows 32 wk + l32 of K/V all share swz(l32)): chunk 2kk + h.
-  uint32_t offq[NKK];
-  {
-    const int sw = swz<CPR>(l32);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) offq[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
-  }
-  const uint32_t rowq = (uint32_t)(32 * half + l32) * RB;
-  const uint32_t rowk = (uint32_t)(32 * wk + l32) * RB;
+  // Per-lane LDS addresses of the 16-byte reads: rows 32 half + l32 of a
+  // Q/dO tile and rows 32 wk + l32 of K/V all have swizzle swz(l32), so
+  // chunk 2kk + h sits at slot 2kk ^ (h ^ swz): byte address base ^ (32 kk).
+  const uint32_t swc = (uint32_t)(h ^ swz<CPR>(l32)) << 4;
+  const uint32_t kbase = lds_addr(sK) + (uint32_t)(32 * wk + l32) * RB + swc;
+  const uint32_t qbase = lds_addr(lds) + 2u * KVB + (uint32_t)(32 * half + l32) * RB + swc;
   // Transposing reads for the dO^T / Q^T operands.
   TrOffsets<DH> tro;
   tro.init(lane);
@@ -431,12 +427,36 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
       f32x16_t sc, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
+      // S and dP interleaved: slot j (k-step j / 2; S = Q K^T for even j,
+      // dP = dO V^T for odd) runs one matrix instruction and requests the
+      // two fragments of slot j + 2 (a ring of three pairs), so no matrix
+      // instruction waits on a fresh LDS read.  The bases are re-derived per
+      // tile (an empty asm hides them from loop-invariant hoisting), so the
+      // per-step addresses are not all held in registers.
+      {
+        uint32_t kb = kbase, qb = qbase + (uint32_t)s * 2u * TB;
+        asm volatile("" : "+v"(kb), "+v"(qb));
+        auto lds16 = [](uint32_t a) __attribute__((always_inline)) {
+          return ld_lds16((const Q3L_LDS void*)(uintptr_t)a);
+        };
+        auto frags = [&](int j, u32x4_t& a, u32x4_t& b) __attribute__((always_inline)) {
+          const uint32_t x = (uint32_t)(32 * (j >> 1));
+          a = lds16((qb ^ x) + (uint32_t)(TB * (j & 1)));     // Q or dO
+          b = lds16((kb ^ x) + (uint32_t)(KVB * (j & 1)));    // K or V
+        };
+        constexpr int NS = 2 * NKK;
+        u32x4_t ra[3], rb[3];
+        frags(0, ra[0], rb[0]);
+        frags(1, ra[1], rb[1]);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4_t ka = ld_lds16(sK + rowk + offq[kk]);
-        const u32x4_t va = ld_lds16(sV + rowk + offq[kk]);
-        sc = mfma32(ld_lds16(sQ + rowq + offq[kk]), ka, sc);
-        dp = mfma32(ld_lds16(sO + rowq + offq[kk]), va, dp);
+        for (int j = 0; j < NS; ++j) {
+          if (j & 1)
+            dp = mfma32(ra[j % 3], rb[j % 3], dp);
+          else
+            sc = mfma32(ra[j % 3], rb[j % 3], sc);
+          if (j + 2 < NS) frags(j + 2, ra[(j + 2) % 3], rb[(j + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // lane: key mykv; rows q = qh0 + 8(e/4) + 4h + e%4 -- four consecutive
       // rows per e/4, so LSE and delta come in float4s.
@@ -569,14 +589,11 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
     load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave, lane);
     load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave, lane);
   };
-  // 16-byte reads of rows 32c + l32 (chunk 2kk + h).
-  uint32_t offk[NKK];
-  {
-    const int sw = swz<CPR>(l32);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) offk[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
-  }
-  const uint32_t rowk = (uint32_t)l32 * RB;
+  // 16-byte reads of rows 32c + l32, chunk 2kk + h, i.e. slot
+  // (2kk + h) ^ swz = 2kk ^ (h ^ swz): byte address kbase ^ (32 kk) (+ the
+  // row block, stage and K/V offsets, multiples of 256 bytes).
+  const uint32_t kbase =
+      lds_addr(lds) + (uint32_t)l32 * RB + ((uint32_t)(h ^ swz<CPR>(l32)) << 4);
   TrOffsets<DH> tro;
   tro.init(lane);
 
@@ -598,14 +615,37 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
       const int kv0 = t * KT;
       f32x16_t sc[2], dp[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) { sc[c][e] = 0.f; dp[c][e] = 0.f; }
+      // S and dP as four interleaved accumulator chains.  Slot j (k-step
+      // j / 4, row block (j / 2) % 2, K for even j, V for odd) runs one
+      // matrix instruction and requests the fragment of slot j + 3 (a ring
+      // of four), so no matrix instruction waits on a fresh LDS read.  The
+      // base address is re-derived per tile (an empty asm hides it from
+      // loop-invariant hoisting), so the 4 NKK addresses are not all held
+      // in registers.
+      {
+        uint32_t fb = kbase + (uint32_t)s * 2u * TB;
+        asm volatile("" : "+v"(fb));
+        auto frag = [&](int j) __attribute__((always_inline)) {
+          const uint32_t a = (fb ^ (uint32_t)(32 * (j >> 2))) +
+                             (uint32_t)(32 * RB * ((j >> 1) & 1) + TB * (j & 1));
+          return ld_lds16((const Q3L_LDS void*)(uintptr_t)a);
+        };
+        constexpr int NS = 4 * NKK;
+        u32x4_t ring[4];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t o = rowk + 32u * RB * c + offk[kk];
-          sc[c] = mfma32(ld_lds16(sK + o), qf[kk], sc[c]);
-          dp[c] = mfma32(ld_lds16(sV + o), of[kk], dp[c]);
+        for (int j = 0; j < 3; ++j) ring[j] = frag(j);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int kk = j >> 2, c = (j >> 1) & 1;
+          if (j & 1)
+            dp[c] = mfma32(ring[j & 3], of[kk], dp[c]);
+          else
+            sc[c] = mfma32(ring[j & 3], qf[kk], sc[c]);
+          if (j + 3 < NS) ring[(j + 3) & 3] = frag(j + 3);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // P in place of S; only tiles that reach the diagonal or the sequence
@@ -627,11 +667,23 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[c][e] = sc[c][e] * (dp[c][e] - dlt);
+      // dQ^T += K^T dS^T: slot j (k-step j / NDT, d block j % NDT) runs one
+      // matrix instruction and requests the transposed K fragment of slot
+      // j + 2 (a ring of three).
+      {
+        constexpr int NQ = 4 * NDT;
+        u32x4_t ring[3];
+        ring[0] = tro.read(sK, 0, 0);
+        ring[1] = tro.read(sK, 1 / NDT, 1 % NDT);
+        u32x4_t df = pack_half(dp[0], 0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t df = pack_half(dp[ks >> 1], ks & 1);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) dqt[dt] = mfma32(tro.read(sK, ks, dt), df, dqt[dt]);
+        for (int j = 0; j < NQ; ++j) {
+          const int ks = j / NDT, dt = j % NDT;
+          if (dt == 0 && j > 0) df = pack_half(dp[ks >> 1], ks & 1);
+          dqt[dt] = mfma32(ring[j % 3], df, dqt[dt]);
+          if (j + 2 < NQ) ring[(j + 2) % 3] = tro.read(sK, (j + 2) / NDT, (j + 2) % NDT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     wait_vmcnt<0>();

@@ -133,6 +133,23 @@ __device__ inline void lds_dma4(uint64_t p, uint32_t voff, uint32_t lds_base) {
                                            voff, 0, 0, 0);
 }
 
+// Buffer resource over [p, p + bytes) (bytes 0: every access is out of
+// range) and 16- / 4-byte accesses through it at a per-lane byte offset.
+// Out-of-range loads (offset kOOB) return zeros and out-of-range stores are
+// dropped, so bounds need no branches.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes = 0x7FFFFFFFu) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4_t buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 template <int N>
 __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -128,8 +128,7 @@ template <class T, int CPL>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     int64_t rows, int n, const T* __restrict__ dy, const T* __restrict__ x,
     const float* __restrict__ rstd, const T* __restrict__ w,
-    const void* __restrict__ resid, int resid_f32, T* __restrict__ dx,
-    float* __restrict__ dx32, float* __restrict__ wpart) {
+    const T* __restrict__ resid, T* __restrict__ dx, float* __restrict__ wpart) {
   extern __shared__ float sdw[];  // [n]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nc = n / 8;
@@ -173,10 +172,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
         V8<T>::load(xr + 8 * ch, b);
         V8<T>::load(w + 8 * ch, ww);
         float rr[8];
-        if (resid_f32) {
-          V8<float>::load(static_cast<const float*>(resid) + row * n + 8 * ch, rr);
-        } else if (resid) {
-          V8<T>::load(static_cast<const T*>(resid) + row * n + 8 * ch, rr);
+        if (resid) {
+          V8<T>::load(resid + row * n + 8 * ch, rr);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) rr[j] = 0.f;
@@ -185,7 +182,6 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
         for (int j = 0; j < 8; ++j)
           o[j] = r * (a[j] * ww[j] - b[j] * r * dot) + rr[j];
         if (dx) V8<T>::store(dx + row * n + 8 * ch, o);
-        if (dx32) V8<float>::store(dx32 + row * n + 8 * ch, o);
       }
     }
   }
@@ -206,121 +202,133 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
   for (int i = threadIdx.x; i < n; i += 256) wpart[(int64_t)blockIdx.x * n + i] = sdw[i];
 }
 
-// bf16 form of the same: a row's dy and x chunks are loaded once, all up
-// front, and kept packed in registers; w is read from LDS for every row.
-// The residual (RK: 0 none, 1 bf16, 2 fp32) is requested with them when it
-// is bf16 (it does not wait for the row reduction); an fp32 residual would
-// need twice the registers and is read after the reduction.
-template <int CPL, int RK>
-__global__ __launch_bounds__(512) void rmsnorm_bwd_bf16_kernel(
+// bf16 form of the same.  A workgroup (4 waves) works on one row at a time,
+// each thread on CPT 8-element chunks (thread t: chunks t, t + 256, ...),
+// and requests the rows it will finish next (dy, x, the residual, rstd)
+// D rows ahead: while a row is reduced and written, the loads of the
+// following D - 1 rows are in flight.  All accesses go through buffer
+// resources, rows past the workgroup's last and chunks past the row at an
+// out-of-range offset (zeros in, stores dropped), so the loop is straight-
+// line code and the compiler's wait counts let the younger rows' loads stay
+// in flight.  The row's dot product is summed over the 4 waves through LDS
+// (one barrier per row, double-buffered by row parity); w and the weight-
+// gradient sums stay in registers for the workgroup's rows, which are
+// blockIdx.x, blockIdx.x + gridDim.x, ...
+template <int CPT, bool RES>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_bf16_kernel(
     int64_t rows, int n, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ x,
     const float* __restrict__ rstd, const bf16_t* __restrict__ w,
-    const void* __restrict__ resid, bf16_t* __restrict__ dx,
-    float* __restrict__ dx32, float* __restrict__ wpart) {
-  extern __shared__ float sdw[];  // [n] dw partial, then w as bf16 [n]
-  bf16_t* sw = reinterpret_cast<bf16_t*>(sdw + n);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // 8 waves
+    const bf16_t* __restrict__ resid, bf16_t* __restrict__ dx, float* __restrict__ wpart) {
+  constexpr int D = CPT <= 2 ? 4 : 2;   // rows in flight
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = n / 8;
-  for (int i = threadIdx.x; i < n; i += 512) sdw[i] = 0.f;
-  for (int i = threadIdx.x; i < nc; i += 512) st16(sw + 8 * i, ld16(w + 8 * i));
-  float acc[CPL][8];
+  const int64_t G = gridDim.x, r0 = blockIdx.x;
+  const int64_t nmine = r0 < rows ? (rows - 1 - r0) / G + 1 : 0;
+  uint32_t coff[CPT];   // byte offset of chunk c in a row, kOOB past the row
+  u32x4_t wv[CPT];
+  float acc[CPT][8];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + 256 * c;
+    coff[c] = ch < nc ? 16u * (uint32_t)ch : kOOB;
+    wv[c] = buf_ld16(buf_rsrc(w), coff[c]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
-  __syncthreads();
-
-  const int64_t nwaves = (int64_t)gridDim.x * 8;
-  for (int64_t row = (int64_t)blockIdx.x * 8 + wave; row < rows; row += nwaves) {
-    // w is re-read from LDS for every row (a compiler barrier keeps its
-    // unpacked copy from being held in registers across rows).
-    asm volatile("" ::: "memory");
-    const float r = rstd[row];
-    u32x4_t ar[CPL], br[CPL], rb[RK == 1 ? CPL : 1];
+  }
+  u32x4_t ra[D][CPT], rb[D][CPT], rr[RES ? D : 1][CPT];
+  float rs[D];
+  auto issue = [&](int64_t i, auto slot) __attribute__((always_inline)) {
+    constexpr int s = decltype(slot)::value;
+    const bool ok = i < nmine;
+    const int64_t ro = (ok ? r0 + i * G : 0) * n;
+    rs[s] = buf_ldf(buf_rsrc(rstd + (ok ? r0 + i * G : 0)), ok ? 0u : kOOB);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < nc) {
-        ar[c] = ld16(dy + row * n + 8 * ch);
-        br[c] = ld16(x + row * n + 8 * ch);
-        if constexpr (RK == 1) rb[c] = ld16(static_cast<const bf16_t*>(resid) + row * n + 8 * ch);
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const uint32_t o = ok ? coff[c] : kOOB;
+      ra[s][c] = buf_ld16(buf_rsrc(dy + ro), o);
+      rb[s][c] = buf_ld16(buf_rsrc(x + ro), o);
+      if constexpr (RES) rr[s][c] = buf_ld16(buf_rsrc(resid + ro), o);
     }
+  };
+  const uint32_t dx_bytes = dx ? 0x7FFFFFFFu : 0u;   // no dx: every store dropped
+  auto finish = [&](int64_t i, auto slot) __attribute__((always_inline)) {
+    constexpr int s = decltype(slot)::value;
+    const bool ok = i < nmine;
+    const int64_t ro = (ok ? r0 + i * G : 0) * n;
+    const float r = rs[s];
     float dot = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if (lane + 64 * c < nc) {
-        const u32x4_t wv = ld16(sw + 8 * (lane + 64 * c));
+    for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pa = ar[c][j >> 1], pb = br[c][j >> 1], pw = wv[j >> 1];
-          const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
-          const float xh = ((j & 1) ? hi_f(pb) : lo_f(pb)) * r;
-          const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
-          dot += a * ww * xh;
-          acc[c][j] += a * xh;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t pa = ra[s][c][j >> 1], pb = rb[s][c][j >> 1], pw = wv[c][j >> 1];
+        const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
+        const float xh = ((j & 1) ? hi_f(pb) : lo_f(pb)) * r;
+        const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
+        dot += a * ww * xh;
+        acc[c][j] += a * xh;
       }
+    // Unpacked copies of dy and x are not kept past the reduction, and the
+    // weight-gradient sums are updated here rather than deferred (the empty
+    // asm marks the registers as rewritten): fewer registers.
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      asm volatile("" : "+v"(ra[s][c]), "+v"(rb[s][c]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(acc[c][j]));
     }
-    // Unpacked copies of dy and x are not kept past the reduction (the empty
-    // asm marks the packed registers as rewritten): half the registers.
+    dot = wave_sum(dot);
+    const int par = (int)(i & 1);
+    if (lane == 0) red[par][wave] = dot;
+    stage_barrier();
+    dot = (red[par][0] + red[par][1] + red[par][2] + red[par][3]) / (float)n;
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dx + ro, dx_bytes);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) asm volatile("" : "+v"(ar[c]), "+v"(br[c]));
-    dot = wave_sum(dot) / (float)n;
+    for (int c = 0; c < CPT; ++c) {
+      float o[8];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < nc) {
-        float rr[8];
-        if constexpr (RK == 2) {
-          const float* rp = static_cast<const float*>(resid) + row * n + 8 * ch;
-          const f32x4_t u = *reinterpret_cast<const f32x4_t*>(rp);
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(rp + 4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) { rr[j] = u[j]; rr[4 + j] = v[j]; }
-        } else if constexpr (RK == 1) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) { rr[2 * j] = lo_f(rb[c][j]); rr[2 * j + 1] = hi_f(rb[c][j]); }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) rr[j] = 0.f;
-        }
-        const u32x4_t wv = ld16(sw + 8 * ch);
-        float o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pa = ar[c][j >> 1], pb = br[c][j >> 1], pw = wv[j >> 1];
-          const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
-          const float b = (j & 1) ? hi_f(pb) : lo_f(pb);
-          const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
-          o[j] = r * (a * ww - b * r * dot) + rr[j];
-        }
-        if (dx)
-          st16(dx + row * n + 8 * ch, u32x4_t{pack2(o[0], o[1]), pack2(o[2], o[3]),
-                                               pack2(o[4], o[5]), pack2(o[6], o[7])});
-        if (dx32) {
-          float* q = dx32 + row * n + 8 * ch;
-          *reinterpret_cast<f32x4_t*>(q) = f32x4_t{o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<f32x4_t*>(q + 4) = f32x4_t{o[4], o[5], o[6], o[7]};
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t pa = ra[s][c][j >> 1], pb = rb[s][c][j >> 1], pw = wv[c][j >> 1];
+        const float a = (j & 1) ? hi_f(pa) : lo_f(pa);
+        const float b = (j & 1) ? hi_f(pb) : lo_f(pb);
+        const float ww = (j & 1) ? hi_f(pw) : lo_f(pw);
+        o[j] = r * (a * ww - b * r * dot);
+        if constexpr (RES) {
+          const uint32_t pr = rr[s][c][j >> 1];
+          o[j] += (j & 1) ? hi_f(pr) : lo_f(pr);
         }
       }
+      buf_st16(rd, ok ? coff[c] : kOOB,
+               u32x4_t{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]),
+                       pack2(o[6], o[7])});
+    }
+    issue(i + D, slot);
+  };
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  if constexpr (D == 4) {
+    issue(2, std::integral_constant<int, 2>{});
+    issue(3, std::integral_constant<int, 3>{});
+  }
+  for (int64_t i = 0; i < nmine; i += D) {
+    finish(i, std::integral_constant<int, 0>{});
+    finish(i + 1, std::integral_constant<int, 1>{});
+    if constexpr (D == 4) {
+      finish(i + 2, std::integral_constant<int, 2>{});
+      finish(i + 3, std::integral_constant<int, 3>{});
     }
   }
-  // Waves add their partials one after another: a fixed summation order, so
-  // the weight gradient is bitwise reproducible.
-  for (int wv = 0; wv < 8; ++wv) {
-    if (wave == wv) {
+  // This workgroup's weight-gradient partial row (its rows summed in order).
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nc)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sdw[8 * ch + j] += acc[c][j];
-      }
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + 256 * c;
+    if (ch < nc) {
+      float* q = wpart + r0 * n + 8 * ch;
+      *reinterpret_cast<f32x4_t*>(q) = f32x4_t{acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
+      *reinterpret_cast<f32x4_t*>(q + 4) = f32x4_t{acc[c][4], acc[c][5], acc[c][6], acc[c][7]};
     }
-    __syncthreads();
   }
-  for (int i = threadIdx.x; i < n; i += 512) wpart[(int64_t)blockIdx.x * n + i] = sdw[i];
 }
 
 constexpr int kNormBwdParts = 512;
@@ -527,43 +535,40 @@ constexpr int kQkBwdParts = 1024;
 
 template <class T>
 hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
-                         const float* rstd, const void* w, const void* resid,
-                         int resid_f32, void* dx, float* dx32, float* wpart,
-                         int* nparts, hipStream_t s) {
+                         const float* rstd, const void* w, const void* resid, void* dx,
+                         float* wpart, int* nparts, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    // At least 8 rows per workgroup, so the loads of the next rows overlap.
+    int64_t grid = cdiv(rows, 8);
+    if (grid > kNormBwdParts) grid = kNormBwdParts;
+    if (grid < 1) grid = 1;
+    *nparts = (int)grid;
+    const int cpt = (int)cdiv(n, 8 * 256);
+#define Q3L_RB16K(C, R)                                                              \
+  hipLaunchKernelGGL((rmsnorm_bwd_bf16_kernel<C, R>), dim3(grid), dim3(256), 0, s,   \
+                     rows, n, (const bf16_t*)dy, (const bf16_t*)x, rstd,             \
+                     (const bf16_t*)w, (const bf16_t*)resid, (bf16_t*)dx, wpart)
+#define Q3L_RB16(C)                \
+  if (resid) Q3L_RB16K(C, true);   \
+  else Q3L_RB16K(C, false);
+    if (cpt <= 1) { Q3L_RB16(1) }
+    else if (cpt <= 2) { Q3L_RB16(2) }
+    else if (cpt <= 4) { Q3L_RB16(4) }
+    else return hipErrorInvalidValue;
+#undef Q3L_RB16
+#undef Q3L_RB16K
+    return hipGetLastError();
+  }
   const int cpl = (int)cdiv(n, 512);
   int64_t grid = cdiv(rows, 4 * 4);  // at least 4 rows per wave
   if (grid > kNormBwdParts) grid = kNormBwdParts;
   if (grid < 1) grid = 1;
   *nparts = (int)grid;
   const size_t shm = (size_t)n * sizeof(float);
-  if constexpr (std::is_same<T, bf16_t>::value) {
-    grid = cdiv(rows, 8 * 4);  // 8 waves per workgroup, at least 4 rows per wave
-    if (grid > kNormBwdParts) grid = kNormBwdParts;
-    if (grid < 1) grid = 1;
-    *nparts = (int)grid;
-#define Q3L_RB16K(C, K)                                                            \
-  hipLaunchKernelGGL((rmsnorm_bwd_bf16_kernel<C, K>), dim3(grid), dim3(512),       \
-                     shm + (size_t)n * 2, s,                                       \
-                     rows, n, (const bf16_t*)dy, (const bf16_t*)x, rstd,           \
-                     (const bf16_t*)w, resid, (bf16_t*)dx, dx32, wpart)
-#define Q3L_RB16(C)                              \
-  if (!resid) Q3L_RB16K(C, 0);                   \
-  else if (!resid_f32) Q3L_RB16K(C, 1);          \
-  else Q3L_RB16K(C, 2);
-    if (cpl <= 1) { Q3L_RB16(1) }
-    else if (cpl <= 2) { Q3L_RB16(2) }
-    else if (cpl <= 4) { Q3L_RB16(4) }
-    else if (cpl <= 8) { Q3L_RB16(8) }
-    else if (cpl <= 16) { Q3L_RB16(16) }
-    else return hipErrorInvalidValue;
-#undef Q3L_RB16
-#undef Q3L_RB16K
-    return hipGetLastError();
-  }
 #define Q3L_RB(C)                                                              \
   hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, C>), dim3(grid), dim3(256), shm, s, \
                      rows, n, (const T*)dy, (const T*)x, rstd, (const T*)w,    \
-                     resid, resid_f32, (T*)dx, dx32, wpart)
+                     (const T*)resid, (T*)dx, wpart)
   if (cpl <= 1) Q3L_RB(1);
   else if (cpl <= 2) Q3L_RB(2);
   else if (cpl <= 4) Q3L_RB(4);
@@ -607,13 +612,11 @@ hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
 
 hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
                        const void* x, const float* rstd, const void* w,
-                       const void* resid, int resid_f32, void* dx,
-                       float* dx32, float* wpart, int* nparts, hipStream_t s) {
+                       const void* resid, void* dx, float* wpart, int* nparts,
+                       hipStream_t s) {
   if (dtype == 1)
-    return rmsnorm_bwd_t<bf16_t>(rows, n, dy, x, rstd, w, resid, resid_f32, dx,
-                                 dx32, wpart, nparts, s);
-  return rmsnorm_bwd_t<float>(rows, n, dy, x, rstd, w, resid, resid_f32, dx,
-                              dx32, wpart, nparts, s);
+    return rmsnorm_bwd_t<bf16_t>(rows, n, dy, x, rstd, w, resid, dx, wpart, nparts, s);
+  return rmsnorm_bwd_t<float>(rows, n, dy, x, rstd, w, resid, dx, wpart, nparts, s);
 }
 
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,

@@ -95,12 +95,10 @@ hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
                        hipStream_t s);
 // dx = resid + rmsnorm_backward(dy);  dw partial sums per block into
 // wpart[nblocks_out][n] (fp32).  Returns the number of partial rows written
-// through *nparts.  resid may be fp32 (resid_f32=1) or dtype; dx_f32 (opt.)
-// receives dx in fp32 as well.
+// through *nparts.  resid (optional) and dx are dtype.
 hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
                        const void* x, const float* rstd, const void* w,
-                       const void* resid, int resid_f32, void* dx,
-                       float* dx_f32, float* wpart, int* nparts,
+                       const void* resid, void* dx, float* wpart, int* nparts,
                        hipStream_t s);
 int rmsnorm_bwd_max_parts();
 // out[n] (+)= sum_p part[p][n]
