@@ -24,6 +24,7 @@
 //     dV^T accumulate in registers, so the G-head sum (adjoint of
 //     repeat_interleave) needs no atomics;
 //   dQ kernel: the forward's shape, accumulating dQ^T over key tiles.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -115,6 +116,11 @@ struct TrOffsets {
   static constexpr int RB = 2 * DH, CPR = RB / 16, NDT = DH / 32;
   uint32_t rowt;
   uint32_t col[2][NDT];
+  // col[i][dt] with rowt added, for dt = 0.  As 4 dt + tc = 4 dt ^ tc, the
+  // chunk slot of column block dt is that of block 0 XOR 4 dt: the byte
+  // offset for block dt is cx[i] ^ 64 dt (rowt and the tile base do not
+  // touch those bits).
+  uint32_t cx[2];
   __device__ void init(int lane) {
     const int g = lane >> 4, sl = lane & 15;
     const int tq = 4 * (g >> 1) + (sl >> 2);
@@ -125,6 +131,16 @@ struct TrOffsets {
       col[0][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq)) << 4);
       col[1][dt] = (uint32_t)(((4 * dt + tc) ^ swz<CPR>(tq + 8)) << 4) + 8u * RB;
     }
+    cx[0] = rowt + col[0][0];
+    cx[1] = rowt + col[1][0];
+  }
+  // The same operand from per-lane bases tb[i] = tile address + cx[i]
+  // (plus a constant `extra`): one XOR per read instead of a held address.
+  __device__ static u32x4_t read_x(const uint32_t (&tb)[2], uint32_t extra, int blk, int dt) {
+    const uint32_t x = 64u * (uint32_t)dt, o = extra + 16u * RB * (uint32_t)blk;
+    const u32x2_t a = ld_tr8((const Q3L_LDS void*)(uintptr_t)((tb[0] ^ x) + o));
+    const u32x2_t b = ld_tr8((const Q3L_LDS void*)(uintptr_t)((tb[1] ^ x) + o));
+    return u32x4_t{a[0], a[1], b[0], b[1]};
   }
   // Operand for 16-row block `blk`, 32-column block dt of tile t.
   __device__ u32x4_t read(const Q3L_LDS char* t, int blk, int dt) const {
@@ -421,80 +437,116 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
     if (it + 1 < total) load_tile(it + 1, s ^ 1);
     const int qh0 = (qt_first + it % nqt) * QT + 32 * half;   // this wave's first row
     // Skip row blocks entirely before this wave's keys (all masked).
-    if (qh0 + 31 >= kw0 && kw0 < L) {
+    // One block of 32 queries x 32 keys as a fixed sequence of slots, each
+    // one matrix instruction plus a share of the vector work that does not
+    // depend on it, pinned by scheduling barriers, so the exponentials and
+    // dS overlap the matrix instructions of the same wave:
+    //   S = Q K^T (NKK slots), then dP = dO V^T (NKK slots) while P =
+    //   exp(S - LSE) is formed; dV^T += dO^T P^T (2 NDT slots) while dS =
+    //   P (dP - D) is formed; dK^T += Q^T dS^T (2 NDT slots).
+    // Fragments are requested two slots ahead (rings of three).  lane: key
+    // mykv; element e holds query row qh0 + 8(e/4) + 4h + e%4 (four
+    // consecutive rows per e/4, so LSE and D come in float4s).  Blocks
+    // that reach the diagonal or the sequence end mask P between the two
+    // phases (one copy of the pinned code; a second copy of it costs more
+    // registers than there are).
+    auto block = [&](bool edge) __attribute__((always_inline)) {
       const Q3L_LDS char* sQ = stage(s);
       const Q3L_LDS char* sO = sQ + TB;
       f32x16_t sc, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
-      // S and dP interleaved: slot j (k-step j / 2; S = Q K^T for even j,
-      // dP = dO V^T for odd) runs one matrix instruction and requests the
-      // two fragments of slot j + 2 (a ring of three pairs), so no matrix
-      // instruction waits on a fresh LDS read.  The bases are re-derived per
-      // tile (an empty asm hides them from loop-invariant hoisting), so the
-      // per-step addresses are not all held in registers.
+      uint32_t kb = kbase, qb = qbase + (uint32_t)s * 2u * TB;
+      asm volatile("" : "+v"(kb), "+v"(qb));
+      auto lds16 = [](uint32_t a) __attribute__((always_inline)) {
+        return ld_lds16((const Q3L_LDS void*)(uintptr_t)a);
+      };
+      // Slot j < NKK: S fragments of k-step j; j >= NKK: dP fragments.
+      auto frags = [&](int j, u32x4_t& fa, u32x4_t& fb) __attribute__((always_inline)) {
+        const int o = j >= NKK;
+        const uint32_t x = (uint32_t)(32 * (j - NKK * o));
+        fa = lds16((qb ^ x) + (uint32_t)(TB * o));     // Q or dO
+        fb = lds16((kb ^ x) + (uint32_t)(KVB * o));    // K or V
+      };
+      const int qr0 = 32 * half + 4 * h;               // row of element 0 in the tile
+      constexpr int EP = 16 / NKK;                     // exponentials per dP slot
+      f32x4_t l4;
       {
-        uint32_t kb = kbase, qb = qbase + (uint32_t)s * 2u * TB;
-        asm volatile("" : "+v"(kb), "+v"(qb));
-        auto lds16 = [](uint32_t a) __attribute__((always_inline)) {
-          return ld_lds16((const Q3L_LDS void*)(uintptr_t)a);
-        };
-        auto frags = [&](int j, u32x4_t& a, u32x4_t& b) __attribute__((always_inline)) {
-          const uint32_t x = (uint32_t)(32 * (j >> 1));
-          a = lds16((qb ^ x) + (uint32_t)(TB * (j & 1)));     // Q or dO
-          b = lds16((kb ^ x) + (uint32_t)(KVB * (j & 1)));    // K or V
-        };
         constexpr int NS = 2 * NKK;
         u32x4_t ra[3], rb[3];
         frags(0, ra[0], rb[0]);
         frags(1, ra[1], rb[1]);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          if (j & 1)
-            dp = mfma32(ra[j % 3], rb[j % 3], dp);
-          else
+          if (j < NKK)
             sc = mfma32(ra[j % 3], rb[j % 3], sc);
+          else
+            dp = mfma32(ra[j % 3], rb[j % 3], dp);
           if (j + 2 < NS) frags(j + 2, ra[(j + 2) % 3], rb[(j + 2) % 3]);
+          if (j >= NKK) {
+#pragma unroll
+            for (int x = 0; x < EP; ++x) {
+              const int e = EP * (j - NKK) + x;
+              if ((e & 3) == 0)
+                l4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qr0 + 8 * (e >> 2)]) * kLog2e;
+              sc[e] = exp2_raw(fmaf(sc[e], p.scale_log2, -l4[e & 3]));
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // lane: key mykv; rows q = qh0 + 8(e/4) + 4h + e%4 -- four consecutive
-      // rows per e/4, so LSE and delta come in float4s.
-      // P in place of S, then dS = P (dP - D); only blocks that reach the
-      // diagonal or the sequence end mask, in a loop of their own.
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int qb = 32 * half + 8 * e4 + 4 * h;
-        const f32x4_t lq = *reinterpret_cast<const f32x4_t*>(&sLD[s][0][qb]) * kLog2e;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sc[4 * e4 + r] = exp2_raw(fmaf(sc[4 * e4 + r], p.scale_log2, -lq[r]));
-      }
-      if ((qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L)) {
+      if (edge) {
+        // Element e (query qh0 + 4h + r) is kept iff mykv <= q < L and
+        // mykv < L, i.e. mlo <= r < mhi.
+        const int mlo = mykv - qh0 - 4 * h;
+        const int mhi = (mykv < L ? L : INT_MIN / 2) - qh0 - 4 * h;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int q = qh0 + 8 * (e >> 2) + 4 * h + (e & 3);
-          sc[e] = (mykv > q || q >= L || mykv >= L) ? 0.f : sc[e];
+          const int r = 8 * (e >> 2) + (e & 3);
+          sc[e] = (r < mlo || r >= mhi) ? 0.f : sc[e];
         }
       }
+      const u32x4_t pf[2] = {pack_half(sc, 0), pack_half(sc, 1)};
+      {
+        constexpr int NT = 4 * NDT;      // dV slots, then dK slots
+        constexpr int DP = 16 / (2 * NDT);   // dS elements per dV slot
+        // Slot j: hk = (j / NDT) % 2, d block j % NDT; dO^T for j < 2 NDT,
+        // Q^T after.
+        uint32_t tb[2] = {lds_addr(sQ) + 32u * RB * half + tro.cx[0],
+                          lds_addr(sQ) + 32u * RB * half + tro.cx[1]};
+        asm volatile("" : "+v"(tb[0]), "+v"(tb[1]));
+        auto trf = [&](int j) __attribute__((always_inline)) {
+          return TrOffsets<DH>::read_x(tb, j < 2 * NDT ? (uint32_t)TB : 0u, (j / NDT) % 2, j % NDT);
+        };
+        u32x4_t rt[3];
+        rt[0] = trf(0);
+        rt[1] = trf(1);
+        u32x4_t df[2];
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int qb = 32 * half + 8 * e4 + 4 * h;
-        const f32x4_t dq4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qb]);
+        for (int j = 0; j < NT; ++j) {
+          const int hk = (j / NDT) % 2, dt = j % NDT;
+          if (j < 2 * NDT)
+            dvt[dt] = mfma32(rt[j % 3], pf[hk], dvt[dt]);
+          else
+            dkt[dt] = mfma32(rt[j % 3], df[hk], dkt[dt]);
+          if (j + 2 < NT) rt[(j + 2) % 3] = trf(j + 2);
+          if (j < 2 * NDT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dp[4 * e4 + r] = sc[4 * e4 + r] * (dp[4 * e4 + r] - dq4[r]);
-      }
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        const u32x4_t pf = pack_half(sc, hk);
-        const u32x4_t df = pack_half(dp, hk);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          dvt[dt] = mfma32(tro.read(sO, 2 * half + hk, dt), pf, dvt[dt]);
-          dkt[dt] = mfma32(tro.read(sQ, 2 * half + hk, dt), df, dkt[dt]);
+            for (int x = 0; x < DP; ++x) {
+              const int e = DP * j + x;
+              if ((e & 3) == 0)
+                l4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qr0 + 8 * (e >> 2)]);
+              dp[e] = sc[e] * (dp[e] - l4[e & 3]);
+            }
+            if (j == 2 * NDT - 1) { df[0] = pack_half(dp, 0); df[1] = pack_half(dp, 1); }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+    };
+    // Row blocks entirely before this wave's keys are skipped (all masked).
+    if (qh0 + 31 >= kw0 && kw0 < L)
+      block((qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L));
     wait_vmcnt<0>();      // this wave's part of tile it+1 has landed
     stage_barrier();      // everyone's part; stage s fully read
   }
