@@ -85,10 +85,40 @@ __device__ inline int swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Rows r0 .. r0+NR-1 (token positions of one sequence starting at token
-// tok0, zero past L) of columns col0 .. col0+DH-1 of a [T][ld] bf16 matrix
-// into an LDS tile in the layout above, by direct loads shared among the NW
-// waves of the workgroup (1 KB per wave-instruction).
+// Direct global->LDS loads of a [NR rows][DH] bf16 tile: rows r0 ..
+// r0+NR-1 of the sequence starting at token tok0 (zeros at rows >= L),
+// columns col0 .. col0+DH-1 of a [T][ld] matrix, into an LDS tile in the
+// layout above, shared among the NW waves of the workgroup (1 KB per
+// wave-instruction).  Instruction j of wave w covers rows RPI (w + NW j) ..
+// +RPI-1; RPI NW is a multiple of 16, so the swizzle of a lane's row, and
+// with it the lane's byte offset, is the same for every j: one per-lane
+// offset, computed once, plus a uniform j (RPI NW ld 2).  Per tile only a
+// buffer resource over the tile's rows is built, ending at row L, so rows
+// past the sequence read zeros without a per-lane test.
+template <int DH, int NR, int NW>
+struct TileLoader {
+  static constexpr int RB = 2 * DH, CPR = RB / 16, RPI = 1024 / RB, NI = NR / RPI / NW;
+  static_assert(NR % (RPI * NW) == 0, "whole instructions per wave");
+  static_assert((RPI * NW) % 16 == 0, "row swizzle independent of the instruction");
+  uint32_t voff;
+  __device__ void init(int64_t ld, int wave, int lane) {
+    const int row = RPI * wave + lane / CPR;
+    voff = (uint32_t)(row * ld * 2) + 16u * (uint32_t)((lane % CPR) ^ swz<CPR>(row));
+  }
+  __device__ void load(const bf16_t* base, int64_t ld, int64_t tok0, int col0, int r0, int L,
+                       Q3L_LDS char* dst, int wave) const {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(
+        base + (tok0 + r0) * ld + col0, (uint32_t)(((int64_t)(L - r0) * ld - col0) * 2));
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      lds_dma16_r(r, voff, (uint32_t)(j * RPI * NW * ld * 2),
+                  uni(lds_addr(dst + 1024 * (wave + NW * j))));
+  }
+};
+
+// The same loads with the per-lane offsets computed per tile (the forward
+// uses this form: holding the offsets costs it more registers than the
+// per-tile address arithmetic costs it time).
 template <int DH, int NR, int NW>
 __device__ inline void load_rows_lds(const bf16_t* base, int64_t ld, int64_t tok0, int col0,
                                      int r0, int L, Q3L_LDS char* dst, int wave, int lane) {
@@ -396,11 +426,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   const int nqt = (L + QT - 1) / QT - qt_first;
   const int total = nqt * p.G;
   auto stage = [&](int s) { return lds + 2 * KVB + s * 2 * TB; };   // Q, then dO
+  TileLoader<DH, QT, 8> qld, old_;
+  qld.init(p.ldq, wave, lane);
+  old_.init(p.lddo, wave, lane);
   auto load_tile = [&](int it, int s) {
     const int head = kvh * p.G + it / nqt;
     const int q0 = (qt_first + it % nqt) * QT;
-    load_rows_lds<DH, QT, 8>(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave, lane);
-    load_rows_lds<DH, QT, 8>(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave, lane);
+    qld.load(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave);
+    old_.load(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave);
     if (wave < 2) {   // log-sum-exp (wave 0) and row sums (wave 1), 64 floats each
       const float* src = wave == 0 ? (const float*)p.lse : p.delta;
       const int q = q0 + lane;
@@ -410,8 +443,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
     }
   };
 
-  load_rows_lds<DH, KB, 8>(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave, lane);
-  load_rows_lds<DH, KB, 8>(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave, lane);
+  {
+    TileLoader<DH, KB, 8> kl, vl;
+    kl.init(p.ldk, wave, lane);
+    vl.init(p.ldv, wave, lane);
+    kl.load(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave);
+    vl.load(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave);
+  }
   load_tile(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
@@ -637,9 +675,12 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   const float dlt = p.delta[sidx];
 
   auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
+  TileLoader<DH, KT, 4> kld, vld;
+  kld.init(p.ldk, wave, lane);
+  vld.init(p.ldv, wave, lane);
   auto load_tile = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave, lane);
-    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave, lane);
+    kld.load(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave);
+    vld.load(p.v, p.ldv, tok0, kvh * DH, t * KT, L, stage(s) + TB, wave);
   };
   // 16-byte reads of rows 32c + l32, chunk 2kk + h, i.e. slot
   // (2kk + h) ^ swz = 2kk ^ (h ^ swz): byte address kbase ^ (32 kk) (+ the

@@ -126,6 +126,12 @@ __device__ inline void lds_dma16(uint64_t p, uint32_t voff, uint32_t soff, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16,
                                            voff, soff, 0, 0);
 }
+// The same through a given buffer resource, at per-lane voff + uniform soff.
+__device__ inline void lds_dma16_r(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                   uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16, voff,
+                                           soff, 0, 0);
+}
 __device__ inline void lds_dma4(uint64_t p, uint32_t voff, uint32_t lds_base) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
