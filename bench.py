@@ -41,10 +41,10 @@ COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 # --kernel-probe`, each scaled by what the same counter reads for the 1 GiB
 # calibration copy.  Valid only for the kernel source it was taken on: the
 # digest below is of gemm_bf16.hip, and a changed source reports null.
-TRAFFIC = {"source_sha256": "f08d3c9541daf827",
-           "fetch_kib": 1181665.4, "write_kib": 590561.9,
-           "copy_fetch_kib": 524303.2, "copy_write_kib": 1048576.0,
-           "bytes": 3024716034}
+TRAFFIC = {"source_sha256": "1312639ac1d64e23",
+           "fetch_kib": 1180825.0, "write_kib": 590462.9,
+           "copy_fetch_kib": 524303.1, "copy_write_kib": 1048576.0,
+           "bytes": 3022893748}
 
 WORKLOADS = {
     "qwen3-8b-bf16-fwd-bwd": 4,
