@@ -596,8 +596,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
                             qkv, m.nqkv, w->q_norm, w->k_norm, rq, rk, cs, sn, dqkv,
                             m.nqkv, qpart, kpart, &np, s));
     if (want_w && c.qk_norm) {
-      Q3L_HIP(reduce_rows(qpart, np, m.dh, grads->q_norm, acc, s));
-      Q3L_HIP(reduce_rows(kpart, np, m.dh, grads->k_norm, acc, s));
+      Q3L_HIP(reduce_rows2(qpart, kpart, np, m.dh, grads->q_norm, grads->k_norm, acc, s));
     }
   }
   // Step 2: dxn = [dq dk dv] [W_q; W_k; W_v].

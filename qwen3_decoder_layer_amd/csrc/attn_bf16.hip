@@ -16,7 +16,8 @@
 //   accumulators.  Output: O (bf16) and the log-sum-exp per query (fp32).
 //
 // Backward (P recomputed from the saved log-sum-exp):
-//   delta = rowsum(dO * O) per query;
+//   delta = rowsum(dO * O) per query, formed by the dQ kernel from the dO
+//     rows it holds anyway (so it runs first);
 //   dK/dV kernel: a workgroup owns 128 keys of one kv head (32 per wave; K
 //     and V in LDS) and sweeps every q head of the group and every query
 //     tile at or after its keys (Q / dO tiles and their LSE / delta by
@@ -49,7 +50,7 @@ struct FwdP {
   // backward
   const bf16_t* dout; int64_t lddo;
   bf16_t* dq; bf16_t* dk; bf16_t* dv;
-  const float* delta;
+  float* delta;   // written by the dQ kernel, read by dK/dV
 };
 
 __device__ inline u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
@@ -363,29 +364,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 }
 
 // ============================ backward ======================================
-// delta[b, h, t] = sum_d dO[t, h, d] * O[t, h, d]
-template <int DH>
-__global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p, float* delta) {
-  constexpr int LP = DH / 8;
-  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
-  const int j = threadIdx.x % LP;
-  const int64_t total = (int64_t)p.B * p.L * p.h_q;
-  const bool valid = item < total;
-  const int64_t it = valid ? item : 0;
-  const int64_t tok = it / p.h_q;
-  const int head = (int)(it % p.h_q);
-  const u32x4_t a = ld16(p.dout + tok * p.lddo + (int64_t)head * DH + 8 * j);
-  const u32x4_t o = ld16(p.o + tok * p.ldo + (int64_t)head * DH + 8 * j);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s += lo_f(a[e]) * lo_f(o[e]) + hi_f(a[e]) * hi_f(o[e]);
-  s = group_sum(s, LP);
-  if (valid && j == 0) {
-    const int64_t b = tok / p.L, t = tok % p.L;
-    delta[(b * p.h_q + head) * p.L + t] = s;
-  }
-}
-
 // dK, dV for 128 keys of one kv head.  Eight waves: wave w owns keys
 // 32 (w % 4) .. +31 and, of every QT-query tile, the 32 query rows
 // 32 (w / 4) .. +31, so the two waves sharing a SIMD work on independent
@@ -672,7 +650,24 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   }
   const int64_t sidx = ((int64_t)b * p.h_q + head) * L + qr;
   const float lse2 = p.lse[sidx] * kLog2e;
-  const float dlt = p.delta[sidx];
+  // D = rowsum(dO * O) of this lane's row: the dO fragments are already in
+  // registers (elements 16 kk + 8h .. +7), O's same elements are loaded, and
+  // the two halves of the row meet across the lane halves.  The dK/dV
+  // kernel, launched after this one, reads D back.
+  float dlt = 0.f;
+  {
+    const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
+    u32x4_t ov[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ov[kk] = ld16(opo + 16 * kk);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
+    dlt += __shfl_xor(dlt, 32, 64);
+    if (h == 0 && qrow < L) p.delta[sidx] = dlt;
+  }
 
   auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
   TileLoader<DH, KT, 4> kld, vld;
@@ -831,19 +826,16 @@ hipError_t attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
 hipError_t attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.L <= 0) return hipSuccess;
   const FwdP p = make_params(a);
-  const int64_t dthreads = (int64_t)p.B * p.L * p.h_q * (a.d_h / 8);
-  dim3 dgrid((unsigned)cdiv(dthreads, 256));
   dim3 kgrid((unsigned)(p.B * p.h_kv), (unsigned)cdiv(p.L, 128));
   const int QB = 32 * p.rb;
   dim3 qgrid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
+  // dQ first: it also writes the row sums D that dK/dV reads.
   if (a.d_h == 128) {
-    hipLaunchKernelGGL(attn_delta_kernel<128>, dgrid, dim3(256), 0, s, p, a.delta);
-    hipLaunchKernelGGL(attn_dkdv_kernel<128>, kgrid, dim3(512), 0, s, p);
     hipLaunchKernelGGL(attn_dq_kernel<128>, qgrid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkdv_kernel<128>, kgrid, dim3(512), 0, s, p);
   } else {
-    hipLaunchKernelGGL(attn_delta_kernel<64>, dgrid, dim3(256), 0, s, p, a.delta);
-    hipLaunchKernelGGL(attn_dkdv_kernel<64>, kgrid, dim3(512), 0, s, p);
     hipLaunchKernelGGL(attn_dq_kernel<64>, qgrid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_dkdv_kernel<64>, kgrid, dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }

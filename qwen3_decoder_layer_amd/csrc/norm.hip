@@ -336,13 +336,18 @@ constexpr int kNormBwdParts = 512;
 // ---- column reduction of partial rows -------------------------------------
 // A workgroup owns 64 columns; its 16 waves sum interleaved sixteenths of
 // the partial rows (lanes over columns: 256-byte coalesced reads), then
-// combine in a fixed order.
+// combine in a fixed order.  One launch may serve two reductions of the same
+// shape (the q and k norm weights): workgroups past the first job's take
+// the second.
 __global__ __launch_bounds__(1024) void reduce_rows_kernel(
-    const float* __restrict__ part, int nparts, int n, float* __restrict__ out,
-    int accumulate) {
+    const float* __restrict__ part, const float* __restrict__ part2, int nparts, int n,
+    float* __restrict__ out, float* __restrict__ out2, int accumulate) {
   __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;   // 16 waves
-  const int i = blockIdx.x * 64 + lane;
+  const int nb = (n + 63) / 64;
+  const bool second = (int)blockIdx.x >= nb;
+  if (second) { part = part2; out = out2; }
+  const int i = ((int)blockIdx.x - (second ? nb : 0)) * 64 + lane;
   float s = 0.f;
   if (i < n) {
 #pragma unroll 8
@@ -622,7 +627,14 @@ hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
                        int accumulate, hipStream_t s) {
   hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)cdiv(n, 64)), dim3(1024),
-                     0, s, part, nparts, n, out, accumulate);
+                     0, s, part, nullptr, nparts, n, out, nullptr, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t reduce_rows2(const float* part, const float* part2, int nparts, int n,
+                        float* out, float* out2, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)(2 * cdiv(n, 64))), dim3(1024),
+                     0, s, part, part2, nparts, n, out, out2, accumulate);
   return hipGetLastError();
 }
 

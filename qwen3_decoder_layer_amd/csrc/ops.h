@@ -104,6 +104,10 @@ int rmsnorm_bwd_max_parts();
 // out[n] (+)= sum_p part[p][n]
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
                        int accumulate, hipStream_t s);
+// Two reductions of the same shape in one launch: out (+)= rows of part,
+// out2 (+)= rows of part2.
+hipError_t reduce_rows2(const float* part, const float* part2, int nparts, int n,
+                        float* out, float* out2, int accumulate, hipStream_t s);
 hipError_t rope_table(int L, int d_h, float theta, float* cos_t, float* sin_t,
                       hipStream_t s);
 // q/k norm + RoPE over the q and k heads of a [T, ld_in] buffer.

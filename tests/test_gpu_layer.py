@@ -78,6 +78,11 @@ SMALL = [
     dict(d=384, h_q=6, h_kv=2, d_h=64, d_ffn=776, B=3, L=129, dtype="bf16",
          qk_norm=False),
     dict(d=256, h_q=2, h_kv=2, d_h=128, d_ffn=256, B=1, L=1, dtype="bf16"),
+    # Widest rows the norms take (8192: four 8-element chunks per thread in
+    # the bf16 RMSNorm backward) and a width whose last chunks overhang the
+    # workgroup (2560), both at token counts that leave partial row groups.
+    dict(d=8192, h_q=4, h_kv=1, d_h=128, d_ffn=384, B=1, L=70, dtype="bf16"),
+    dict(d=2560, h_q=4, h_kv=2, d_h=64, d_ffn=512, B=2, L=45, dtype="bf16"),
 ]
 
 
