@@ -650,25 +650,6 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
   }
   const int64_t sidx = ((int64_t)b * p.h_q + head) * L + qr;
   const float lse2 = p.lse[sidx] * kLog2e;
-  // D = rowsum(dO * O) of this lane's row: the dO fragments are already in
-  // registers (elements 16 kk + 8h .. +7), O's same elements are loaded, and
-  // the two halves of the row meet across the lane halves.  The dK/dV
-  // kernel, launched after this one, reads D back.
-  float dlt = 0.f;
-  {
-    const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
-    u32x4_t ov[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) ov[kk] = ld16(opo + 16 * kk);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
-    dlt += __shfl_xor(dlt, 32, 64);
-    if (h == 0 && qrow < L) p.delta[sidx] = dlt;
-  }
-
   auto stage = [&](int s) { return lds + s * 2 * TB; };   // K, then V
   TileLoader<DH, KT, 4> kld, vld;
   kld.init(p.ldk, wave, lane);
@@ -691,7 +672,27 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqt[dt][e] = 0.f;
 
-  load_tile(0, 0);
+  // D = rowsum(dO * O) of this lane's row: the dO fragments are already in
+  // registers (elements 16 kk + 8h .. +7), O's same elements are loaded, and
+  // the two halves of the row meet across the lane halves.  The dK/dV
+  // kernel, launched after this one, reads D back.  The first K/V tile is
+  // requested between the loads of O and their use, so it overlaps this.
+  float dlt = 0.f;
+  {
+    const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
+    u32x4_t ov[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ov[kk] = ld16(opo + 16 * kk);
+    load_tile(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
+    dlt += __shfl_xor(dlt, 32, 64);
+    if (h == 0 && qrow < L) p.delta[sidx] = dlt;
+  }
+
   wait_vmcnt<0>();
   stage_barrier();
   for (int t = 0; t < ntiles; ++t) {
