@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define Q3L_VERSION 1
+#define Q3L_VERSION 2
 
 typedef enum { Q3L_F32 = 0, Q3L_BF16 = 1 } q3l_dtype;
 
@@ -123,6 +123,14 @@ typedef struct {
   size_t gu;       /* [T, 2*d_ffn] dtype: gate in columns [0, d_ffn), up in
                       [d_ffn, 2*d_ffn)                                     */
   size_t f;        /* [T, d_ffn] dtype, silu(gate) * up                    */
+  size_t wt;       /* bf16 only (empty for fp32): the projection weights
+                      transposed to [in, out] for the backward's input-
+                      gradient GEMMs: W_down^T [d_ffn, d], then [W_gate;
+                      W_up]^T [d, 2*d_ffn], W_o^T [q_d, d], [W_q; W_k;
+                      W_v]^T [d, q_d + 2*kv_d] (q_d = h_q*d_h, kv_d =
+                      h_kv*d_h), each 256-byte aligned                    */
+  size_t xnt;      /* bf16 only (empty for fp32): xn^T [d, T8] with T8 = T
+                      rounded up to a multiple of 8, columns >= T zero     */
   size_t total;    /* bytes of the whole buffer                            */
 } q3l_saved_layout;
 
@@ -149,7 +157,13 @@ size_t q3l_workspace_bytes(const q3l_layer_cfg *cfg, int backward);
  *             outlive that call, and x and the weights must not change in
  *             between.
  *   workspace q3l_workspace_bytes(cfg, 0) bytes of scratch (contents
- *             undefined afterwards); workspace_bytes is its size. */
+ *             undefined afterwards); workspace_bytes is its size.
+ * With bf16 and `saved`, the transposed copies (wt, xnt above) are written
+ * by a second stream the library owns (one per device, created on first
+ * use, default priority), forked from `stream` with an event before the
+ * attention step and joined back into `stream` after it: all work of the
+ * call is still ordered on `stream`, and the pattern can be captured into a
+ * HIP graph. */
 q3l_status q3l_layer_forward(const q3l_layer_cfg *cfg, const q3l_weights *w,
                              const void *x, const q3l_outputs *out,
                              void *saved, void *workspace,

@@ -43,7 +43,7 @@ class Outputs(C.Structure):
 
 SAVED_FIELDS = ("rstd1", "xn", "qkv", "qk_rope", "rstd_q", "rstd_k",
                 "rope_cos", "rope_sin", "attn_o", "lse", "h", "rstd2", "hn",
-                "gu", "f", "total")
+                "gu", "f", "wt", "xnt", "total")
 
 
 class SavedLayout(C.Structure):

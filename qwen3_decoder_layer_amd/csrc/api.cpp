@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/q3layer.h"
@@ -124,15 +125,41 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
   s.hn = take(m.T * m.d * m.es);
   s.gu = take(m.T * 2 * (size_t)m.ffn * m.es);
   s.f = take(m.T * (size_t)m.ffn * m.es);
+  // Transposed copies for the backward (bf16): the weights, then xn^T.
+  s.wt = off;
+  if (c.dtype == Q3L_BF16) {
+    take((size_t)m.ffn * m.d * 2);
+    take((size_t)m.d * 2 * m.ffn * 2);
+    take((size_t)m.qd * m.d * 2);
+    take((size_t)m.d * m.nqkv * 2);
+  }
+  s.xnt = off;
+  if (c.dtype == Q3L_BF16) take((size_t)m.d * ((m.T + 7) / 8 * 8) * 2);
   s.total = off;
   return s;
 }
 
+// Offsets of the four transposed weights inside the saved wt region.
+struct WtLayout { size_t down, gu, o, qkv; };
+WtLayout wt_layout(const q3l_layer_cfg& c) {
+  const size_t ffn = (size_t)c.d_ffn, d = (size_t)c.d;
+  const size_t qd = (size_t)c.h_q * c.d_h, nqkv = qd + 2 * (size_t)c.h_kv * c.d_h;
+  WtLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+  w.down = take(ffn * d * 2);
+  w.gu = take(d * 2 * ffn * 2);
+  w.o = take(qd * d * 2);
+  w.qkv = take(d * nqkv * 2);
+  return w;
+}
+
 struct BwdWs {
   size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
-  // bf16 only: transposed weights ([in, out]) and three scratch buffers for
-  // the transposed operands of the weight-gradient GEMMs ([features, Tp]).
-  size_t wt_down, wt_gu, wt_o, wt_qkv, tA, tB, tC;
+  // bf16 only: three scratch buffers for the transposed operands of the
+  // weight-gradient GEMMs ([features, Tp]).  (The transposed weights are in
+  // the saved block.)
+  size_t tA, tB, tC;
   size_t total;
 };
 
@@ -156,10 +183,6 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
   w.kpart = take((size_t)qknorm_bwd_max_parts() * m.dh * 4);
   if (c.dtype == Q3L_BF16) {
     const size_t Tp = (size_t)pad8(m.T);
-    w.wt_down = take((size_t)m.ffn * m.d * 2);
-    w.wt_gu = take((size_t)m.d * 2 * m.ffn * 2);
-    w.wt_o = take((size_t)m.qd * m.d * 2);
-    w.wt_qkv = take((size_t)m.d * m.nqkv * 2);
     w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
     w.tB = take((size_t)std::max<int64_t>(std::max<int64_t>(m.ffn, m.qd), m.d) * Tp * 2);
     w.tC = take((size_t)m.d * Tp * 2);
@@ -264,6 +287,61 @@ q3l_status q3l_saved_layout_of(const q3l_layer_cfg* cfg, q3l_saved_layout* out) 
   return Q3L_OK;
 }
 
+// ---- second stream ------------------------------------------------------
+// One per device, created on first use and kept for the process: work that
+// only depends on the call's inputs (the backward's transposed copies) runs
+// on it beside the attention step, forked from and joined back into the
+// caller's stream with events.  Default priority.  The mutex keeps one
+// call's record / wait pairs together when several host threads share a
+// device.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& sd = g_side[dev];
+  if (!sd.s) {
+    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+  }
+  *out = &sd;
+  return hipSuccess;
+}
+
+// The copies the bf16 backward reads in K-contiguous form, from inputs the
+// forward already has: the seven projection weights transposed to [in, out]
+// (one launch), and xn^T [d, Tp].
+hipError_t transposed_copies(const q3l_layer_cfg& c, const q3l_weights* w, const void* xn,
+                             char* wt, char* xnt, hipStream_t s) {
+  const Dims m = dims_of(c);
+  const WtLayout o = wt_layout(c);
+  const int d = m.d, ffn = m.ffn, qd = m.qd, kvd = m.kvd;
+  const int T = (int)m.T, Tp = (int)((m.T + 7) / 8 * 8);
+  char* wt_down = wt + o.down;
+  char* wt_gu = wt + o.gu;
+  char* wt_o = wt + o.o;
+  char* wt_qkv = wt + o.qkv;
+  const TransposeJob jobs[8] = {
+      {w->down, ffn, wt_down, d, d, d, ffn},
+      {w->gate, d, wt_gu, 2 * (int64_t)ffn, ffn, ffn, d},
+      {w->up, d, wt_gu + (size_t)ffn * 2, 2 * (int64_t)ffn, ffn, ffn, d},
+      {w->o, qd, wt_o, d, d, d, qd},
+      {w->q, d, wt_qkv, m.nqkv, qd, qd, d},
+      {w->k, d, wt_qkv + (size_t)qd * 2, m.nqkv, kvd, kvd, d},
+      {w->v, d, wt_qkv + (size_t)(qd + kvd) * 2, m.nqkv, kvd, kvd, d},
+      {xn, d, xnt, Tp, T, Tp, d}};
+  return transpose_bf16_batch(jobs, 8, s);
+}
+
 size_t q3l_saved_bytes(const q3l_layer_cfg* cfg) {
   if (validate(cfg) != Q3L_OK) return 0;
   return saved_layout(*cfg).total;
@@ -271,7 +349,9 @@ size_t q3l_saved_bytes(const q3l_layer_cfg* cfg) {
 
 size_t q3l_workspace_bytes(const q3l_layer_cfg* cfg, int backward) {
   if (validate(cfg) != Q3L_OK) return 0;
-  return backward ? bwd_layout(*cfg).total : saved_layout(*cfg).total;
+  // Forward without `saved`: room for the intermediates up to (not
+  // including) the backward's transposed copies.
+  return backward ? bwd_layout(*cfg).total : saved_layout(*cfg).wt;
 }
 
 q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
@@ -295,9 +375,9 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     Q3L_CHECK_PTR(S, "saved");
   } else {
     Q3L_CHECK_PTR(workspace, "workspace");
-    if (workspace_bytes < L.total)
+    if (workspace_bytes < L.wt)
       return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes,
-                  L.total);
+                  L.wt);
     S = workspace;
   }
   const Dims m = dims_of(c);
@@ -345,7 +425,27 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.k = static_cast<const char*>(qkr) + (size_t)m.qd * m.es; a.ldk = m.nqk;
     a.v = qkvp + (size_t)(m.qd + m.kvd) * m.es; a.ldv = m.nqkv;
     a.o = ao; a.ldo = m.qd; a.lse = lse;
-    Q3L_HIP(attn_fwd(dt, a, s));
+    if (dt == Q3L_BF16 && saved) {
+      // The backward's transposed copies on the second stream, beside the
+      // attention kernel (which leaves registers and bandwidth to spare).
+      std::lock_guard<std::mutex> lk(g_side_mu);
+      SideStream* sd = nullptr;
+      Q3L_HIP(side_stream(&sd));
+      Q3L_HIP(hipEventRecord(sd->fork, s));
+      Q3L_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
+      const hipError_t e1 = transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), sd->s);
+      const hipError_t e2 = hipEventRecord(sd->join, sd->s);
+      const hipError_t e3 = attn_fwd(dt, a, s);
+      // Joined whatever happened above, so nothing of this call is left
+      // running unordered with the caller's stream.
+      const hipError_t e4 = hipStreamWaitEvent(s, sd->join, 0);
+      Q3L_HIP(e1);
+      Q3L_HIP(e2);
+      Q3L_HIP(e3);
+      Q3L_HIP(e4);
+    } else {
+      Q3L_HIP(attn_fwd(dt, a, s));
+    }
   }
   // Steps 6-7: o_proj with the residual in the epilogue.
   {
@@ -464,25 +564,18 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   // (T padded to a multiple of 8 with zeros) into reused scratch buffers.
   const bool bt = dt == Q3L_BF16;
   const int Tp = (int)pad8(m.T);
-  char* wt_down = bt ? at(workspace, W.wt_down) : nullptr;
-  char* wt_gu = bt ? at(workspace, W.wt_gu) : nullptr;
-  char* wt_o = bt ? at(workspace, W.wt_o) : nullptr;
-  char* wt_qkv = bt ? at(workspace, W.wt_qkv) : nullptr;
+  // The transposed weights and xn^T were written by the forward into the
+  // saved block.
+  const WtLayout WT = wt_layout(c);
+  const char* wtb = bt ? at(saved, L.wt) : nullptr;
+  const char* wt_down = bt ? wtb + WT.down : nullptr;
+  const char* wt_gu = bt ? wtb + WT.gu : nullptr;
+  const char* wt_o = bt ? wtb + WT.o : nullptr;
+  const char* wt_qkv = bt ? wtb + WT.qkv : nullptr;
+  const char* xnt = bt ? at(saved, L.xnt) : nullptr;
   char* tA = bt ? at(workspace, W.tA) : nullptr;
   char* tB = bt ? at(workspace, W.tB) : nullptr;
   char* tC = bt ? at(workspace, W.tC) : nullptr;
-  if (bt) {   // the seven weight transposes, one launch
-    const int d = m.d, ffn = m.ffn, qd = m.qd, kvd = m.kvd;
-    const TransposeJob jobs[7] = {
-        {w->down, ffn, wt_down, d, d, d, ffn},
-        {w->gate, d, wt_gu, 2 * (int64_t)ffn, ffn, ffn, d},
-        {w->up, d, wt_gu + (size_t)ffn * 2, 2 * (int64_t)ffn, ffn, ffn, d},
-        {w->o, qd, wt_o, d, d, d, qd},
-        {w->q, d, wt_qkv, m.nqkv, qd, qd, d},
-        {w->k, d, wt_qkv + (size_t)qd * 2, m.nqkv, kvd, kvd, d},
-        {w->v, d, wt_qkv + (size_t)(qd + kvd) * 2, m.nqkv, kvd, kvd, d}};
-    Q3L_HIP(transpose_bf16_batch(jobs, 7, s));
-  }
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
   // feature counts; A/B activations with row strides lda/ldb).  bf16: A and
   // B are transposed into tA and tB (tA_, tB_ when given); a_done / b_done
@@ -619,7 +712,9 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     e.cs[1] = grads->k; e.cstart[1] = m.qd;
     e.cs[2] = grads->v; e.cstart[2] = m.qd + m.kvd;
     e.cnseg = 3;
-    Q3L_HIP(wgrad(dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e));
+    // bf16: xn^T is in the saved block (written by the forward).
+    Q3L_HIP(wgrad(dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e, false, bt, nullptr,
+                  const_cast<char*>(xnt)));
   }
   // Step 1: input RMSNorm adjoint plus the attention residual dh.
   {
