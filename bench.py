@@ -84,7 +84,13 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     W = {n: up(inp[n]) for n in synth.PARAM_NAMES}
     x = up(inp["x"])
     backward = cfg["backward"]
-    saved = torch.empty(q3.saved_bytes(lc), dtype=torch.uint8, device=dev)
+    # A training step saves the intermediates for its backward; a forward-only
+    # workload runs as inference, with scratch instead (allocated here, not in
+    # the timed loop).
+    saved = (torch.empty(q3.saved_bytes(lc), dtype=torch.uint8, device=dev)
+             if backward else None)
+    fwd_ws = (None if backward else
+              torch.empty(q3.workspace_bytes(lc, False), dtype=torch.uint8, device=dev))
     out = {}
     if cfg.get("tp_partial"):
         out = {k: torch.empty((lc.B, lc.L, lc.d), dtype=torch.float32, device=dev)
@@ -101,7 +107,7 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     stream = torch.cuda.current_stream()
 
     def step():
-        q3.layer_forward(lc, W, x, out=out, saved=saved, stream=stream)
+        q3.layer_forward(lc, W, x, out=out, saved=saved, workspace=fwd_ws, stream=stream)
         if backward:
             q3.layer_backward(lc, W, x, dy, saved, dx=dx, grads=grads,
                               workspace=ws, stream=stream)
@@ -116,7 +122,7 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     elapsed = time.perf_counter() - t0
 
     k_ms = time_dominant(lc, W["gate"], W["up"], stream, max(10, steps), between=step)
-    del saved
+    del saved, fwd_ws
     return {"elapsed": elapsed, "kernel_ms": k_ms}
 
 
