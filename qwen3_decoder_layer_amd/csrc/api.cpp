@@ -307,6 +307,7 @@ hipError_t side_stream(SideStream** out) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_side_mu);
   SideStream& sd = g_side[dev];
   if (!sd.s) {
     if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
@@ -400,6 +401,10 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   void* f = at(S, L.f);
   const char* qkvp = static_cast<const char*>(qkv);
 
+  // The second stream (bf16 training forward) is obtained before anything
+  // is enqueued, so a failure to create it leaves no work behind.
+  SideStream* sd = nullptr;
+  if (dt == Q3L_BF16 && saved) Q3L_HIP(side_stream(&sd));
   // Step 1: input RMSNorm.
   Q3L_HIP(rmsnorm_fwd(dt, m.T, m.d, x, w->in_norm, c.eps, xn, rstd1, s));
   // Step 2: q/k/v projections as one GEMM over the stacked weights.
@@ -425,12 +430,11 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.k = static_cast<const char*>(qkr) + (size_t)m.qd * m.es; a.ldk = m.nqk;
     a.v = qkvp + (size_t)(m.qd + m.kvd) * m.es; a.ldv = m.nqkv;
     a.o = ao; a.ldo = m.qd; a.lse = lse;
-    if (dt == Q3L_BF16 && saved) {
+    if (sd) {
       // The backward's transposed copies on the second stream, beside the
-      // attention kernel (which leaves registers and bandwidth to spare).
+      // attention kernel.  The lock keeps this call's record / wait pairs on
+      // the shared events together.
       std::lock_guard<std::mutex> lk(g_side_mu);
-      SideStream* sd = nullptr;
-      Q3L_HIP(side_stream(&sd));
       Q3L_HIP(hipEventRecord(sd->fork, s));
       Q3L_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
       const hipError_t e1 = transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), sd->s);
