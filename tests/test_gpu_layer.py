@@ -288,3 +288,59 @@ def test_preset4_qwen3_8b_forward_backward_golden():
         errs[name + "_maxabs"] = abs(np.max(np.abs(a)) / float(gold[f"{name}_maxabs"]) - 1)
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+def test_other_stream_and_graph_replay():
+    """The forward forks work to the library's second stream and joins it
+    back: results on another caller stream and from a replayed HIP graph of
+    forward + backward are bitwise those of the eager default-stream run."""
+    need_gpu()
+    import torch
+    say("caller stream / graph replay")
+    cfg = synth.make_cfg(d=256, h_q=4, h_kv=2, d_h=64, d_ffn=512, B=2, L=96,
+                         dtype="bf16")
+    inp = synth.make_inputs(cfg, 21, with_dy=True)
+    c = q3.LayerConfig.from_dict(cfg)
+    W = gpu_weights(inp, "bf16")
+    x, dy = dev(inp["x"], "bf16"), dev(inp["dy"], "bf16")
+    saved = torch.empty(q3.saved_bytes(c), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(q3.workspace_bytes(c, True), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty(W[n].shape, dtype=torch.float32, device="cuda")
+             for n in synth.PARAM_NAMES}
+
+    def step(stream):
+        q3.layer_forward(c, W, x, out={"y": y}, saved=saved, stream=stream)
+        q3.layer_backward(c, W, x, dy, saved, dx=dx, grads=grads, workspace=ws,
+                          stream=stream)
+
+    def snapshot():
+        return [t.clone() for t in [y, dx] + [grads[n] for n in synth.PARAM_NAMES]]
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = snapshot()
+
+    side = torch.cuda.Stream()
+    for t in [y, dx] + list(grads.values()):
+        t.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        step(side)
+    side.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(snapshot(), ref))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(3):
+        for t in [y, dx] + list(grads.values()):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep}"
+        step(torch.cuda.current_stream())   # eager work between replays
+        torch.cuda.synchronize()
