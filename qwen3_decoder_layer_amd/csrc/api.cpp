@@ -563,9 +563,10 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   const int T = (int)m.T;
 
   // bf16: every backward GEMM runs in the matrix-core kernel's K-contiguous
-  // form.  Weights are transposed to [in, out] once per call; the two
-  // operands of each weight-gradient GEMM are transposed to [features, T]
-  // (T padded to a multiple of 8 with zeros) into reused scratch buffers.
+  // form.  The weights transposed to [in, out], and xn^T, come from the
+  // saved block (the forward wrote them); the other operands of the
+  // weight-gradient GEMMs are transposed to [features, T] (T padded to a
+  // multiple of 8 with zeros) into reused scratch buffers.
   const bool bt = dt == Q3L_BF16;
   const int Tp = (int)pad8(m.T);
   // The transposed weights and xn^T were written by the forward into the
