@@ -310,9 +310,20 @@ hipError_t side_stream(SideStream** out) {
   std::lock_guard<std::mutex> lk(g_side_mu);
   SideStream& sd = g_side[dev];
   if (!sd.s) {
-    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    // All three or none: a partial failure releases what was created.
+    hipEvent_t f = nullptr, j = nullptr;
+    hipStream_t st = nullptr;
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) == hipSuccess) {
+      sd.fork = f;
+      sd.join = j;
+      sd.s = st;
+    } else {
+      if (f) (void)hipEventDestroy(f);
+      if (j) (void)hipEventDestroy(j);
+      return e;
+    }
   }
   *out = &sd;
   return hipSuccess;
@@ -569,8 +580,6 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   // multiple of 8 with zeros) into reused scratch buffers.
   const bool bt = dt == Q3L_BF16;
   const int Tp = (int)pad8(m.T);
-  // The transposed weights and xn^T were written by the forward into the
-  // saved block.
   const WtLayout WT = wt_layout(c);
   const char* wtb = bt ? at(saved, L.wt) : nullptr;
   const char* wt_down = bt ? wtb + WT.down : nullptr;
