@@ -121,3 +121,48 @@ def test_attention_strided_views():
     O_ref, _ = oracle.attention(qq, kk, vv)
     assert rel_err(host(o).reshape(O_ref.shape), O_ref) <= TOL["bf16"]
     torch.cuda.synchronize()
+
+
+# Logits whose scale grows along the sequence: the log-sum-exp of the last
+# rows reaches 55-75 in log2 units, against under 10 for the first. The
+# kernels' running maximum then moves many times within a row and the partial
+# output and row sum are rescaled each time (the block-state merge of the
+# online softmax, state-placement page, section 4.2); the result must still be
+# the one-pass softmax of the oracle. A CPU emulation of the kernels' bf16
+# roundings on these inputs stays within 5e-3 of the oracle.
+GROWING = [
+    # q scale, growth of the key scale from the first to the last position
+    (1.0, 10.0),
+    (3.0, 4.0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("qs,kgrow", GROWING, ids=["keys-growing", "sharp-growing"])
+def test_attention_growing_logits(dtype, qs, kgrow):
+    need_gpu()
+    B, L, hq, hkv, dh = 1, 400, 4, 2, 128
+    say(f"attention growing logits {dtype} qs={qs} kgrow={kgrow} B={B} L={L}")
+    rng = np.random.default_rng(11)
+    ramp = (1.0 + kgrow * np.arange(L) / L)[None, :, None, None]
+    q = _rand(rng, (B, L, hq, dh), qs, dtype)
+    k = (rng.standard_normal((B, L, hkv, dh)) * ramp).astype(np.float32)
+    k = synth.bf16_round(k) if dtype == "bf16" else k
+    v = _rand(rng, (B, L, hkv, dh), 1.0, dtype)
+    do = _rand(rng, (B, L, hq, dh), 1.0, dtype)
+    q64, k64, v64 = (t.astype(np.float64) for t in (q, k, v))
+    O_ref, lse_ref = oracle.attention(q64, k64, v64)
+    # The inputs must reach the regime this test is for.
+    assert np.max(lse_ref) * np.log2(np.e) > 50.0
+    gq = dev(q.reshape(B, L, hq * dh), dtype)
+    gk = dev(k.reshape(B, L, hkv * dh), dtype)
+    gv = dev(v.reshape(B, L, hkv * dh), dtype)
+    o, lse = q3.attention_fwd(gq, gk, gv, hq, hkv, dh)
+    assert rel_err(host(o).reshape(O_ref.shape), O_ref) <= TOL[dtype]
+    assert np.max(np.abs(host(lse) - lse_ref)) <= 1e-3 * max(1.0, np.max(np.abs(lse_ref)))
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(do.astype(np.float64), q64, k64, v64)
+    dq, dk, dv = q3.attention_bwd(gq, gk, gv, o, dev(do.reshape(B, L, hq * dh), dtype),
+                                  lse, hq, hkv, dh)
+    assert rel_err(host(dq).reshape(dq_ref.shape), dq_ref) <= TOL[dtype]
+    assert rel_err(host(dk).reshape(dk_ref.shape), dk_ref) <= TOL[dtype]
+    assert rel_err(host(dv).reshape(dv_ref.shape), dv_ref) <= TOL[dtype]
