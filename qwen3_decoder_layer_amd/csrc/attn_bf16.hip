@@ -303,7 +303,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
         row_max(std::true_type{});
       else
         row_max(std::false_type{});
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * p.scale_log2;   // log2 units
+      // The two half-waves hold the two key halves of a query: exchange their
+      // maxima with a lane swap between the halves (a VALU op, no LDS queue).
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+        mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.scale_log2;   // log2 units
+      }
       // The reference maximum m_run moves (and O, l are rescaled) only when a
       // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
       // the result is exact, and the 64-multiply rescale is usually skipped.
@@ -330,8 +336,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
           cur[c][e] = pv;
           rs += pv;
         }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run += rs;
+      l_run += rs;   // this half-wave's keys; the halves are added at the end
       const Q3L_LDS char* sV = vslot(s);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -348,6 +353,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     if (t + 1 < ntiles) iter(t + 1, std::integral_constant<int, 1>{});
   }
 
+  l_run += __shfl_xor(l_run, 32, 64);
   if (qrow >= L) return;
   const float inv = 1.0f / l_run;
   bf16_t* op = p.o + (tok0 + qrow) * p.ldo + (int64_t)head * DH;
