@@ -9,11 +9,13 @@ eleven fp32 weight gradients), on the Qwen3-8B-shaped layer (d=4096, 32 q /
 8 kv heads, d_h=128, d_ffn=12288, B=2, L=4096, bf16).  Inputs and weights
 are resident in HBM before the timed region.  Rank 0 prints one JSON line.
 
-Besides the step timing it measures, with HIP events on the stream the
-library launches on, the dominant kernel (the fused gate/up GEMM with the
-SwiGLU epilogue, launched through its phase-level entry point with the
-layer's shapes), and times the fp64 CPU oracle on a bounded sample of the
-same workload as a reported baseline.
+After the timed steps it runs the same number of steps again with phase
+marks: HIP events the library records on its stream at every phase
+boundary.  Their medians give each phase's time and its fraction of the
+matrix-core or HBM roofline ("phases"), and the in-step time of the dominant
+kernel (the fused gate/up GEMM with the SwiGLU epilogue) for "roofline".  The
+fp64 CPU oracle is timed on a bounded sample of the same workload as a
+reported baseline.
 """
 from __future__ import annotations
 
@@ -71,6 +73,53 @@ def model_flops(c: dict, backward: bool) -> dict:
     return out
 
 
+def phase_work(c: dict) -> tuple:
+    """Algorithmic work of each phase of one step, keyed by the library's
+    phase names: (bound, amount) with bound "mfma" (FLOPs) or "hbm" (bytes:
+    one read of each input and one write of each output).  Attention counts
+    causal pairs (model FLOPs: 4 h_q d_h per pair forward, twice that
+    backward; the recomputed scores are not counted)."""
+    T, d, f, L = c["B"] * c["L"], c["d"], c["d_ffn"], c["L"]
+    qd, kvd, dh = c["h_q"] * c["d_h"], c["h_kv"] * c["d_h"], c["d_h"]
+    nqkv, nqk, heads = qd + 2 * kvd, qd + kvd, c["h_q"] + c["h_kv"]
+    pairs = c["B"] * L * (L + 1) // 2
+    a = 2                                   # bf16 bytes
+    w_bytes = a * (d * nqkv + qd * d + 3 * d * f)
+    norm_fwd = ("hbm", 2 * a * T * d + 4 * T + a * d)
+    norm_bwd = ("hbm", 4 * a * T * d + 4 * T + a * d)
+    fwd = {
+        "F1 rmsnorm": norm_fwd,
+        "F2 qkv gemm": ("mfma", 2 * T * d * nqkv),
+        "F3-F4 qk-norm + rope": ("hbm", 2 * a * T * nqk + 4 * T * heads + 8 * L * dh),
+        "transposes for the backward": ("hbm", 2 * w_bytes + 2 * a * T * d),
+        "F5 attention": ("mfma", 4 * c["h_q"] * dh * pairs),
+        "F6 o gemm + residual": ("mfma", 2 * T * qd * d),
+        "F7 rmsnorm": norm_fwd,
+        "F8-F9 gate/up gemm + swiglu": ("mfma", 2 * T * d * 2 * f),
+        "F10 down gemm + residual": ("mfma", 2 * T * f * d),
+    }
+    bwd = {
+        "B1 down dgrad gemm": ("mfma", 2 * T * d * f),
+        "B2 swiglu adjoint": ("hbm", 8 * a * T * f),
+        "B1 down wgrad transposes": ("hbm", 2 * a * T * d),
+        "B1 down wgrad gemm": ("mfma", 2 * T * d * f),
+        "B3 gate/up dgrad gemm": ("mfma", 2 * T * 2 * f * d),
+        "B3 gate/up wgrad transposes": ("hbm", 2 * a * T * d),
+        "B3 gate/up wgrad gemm": ("mfma", 2 * T * 2 * f * d),
+        "B4 rmsnorm bwd": norm_bwd,
+        "B5 o dgrad gemm": ("mfma", 2 * T * d * qd),
+        "B5 o wgrad transposes": ("hbm", 2 * a * T * (d + qd)),
+        "B5 o wgrad gemm": ("mfma", 2 * T * d * qd),
+        "B6 attention bwd": ("mfma", 8 * c["h_q"] * dh * pairs),
+        "B7 qk-norm + rope bwd": ("hbm", 3 * a * T * nqk + 4 * T * heads),
+        "B8 qkv dgrad gemm": ("mfma", 2 * T * nqkv * d),
+        "B8 qkv wgrad transposes": ("hbm", 2 * a * T * nqkv),
+        "B8 qkv wgrad gemm": ("mfma", 2 * T * nqkv * d),
+        "B9 rmsnorm bwd": norm_bwd,
+    }
+    return fwd, bwd
+
+
 def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     import torch
     import qwen3_decoder_layer_amd as q3
@@ -105,12 +154,20 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
         ws = torch.empty(q3.workspace_bytes(lc, True), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
+    # The training forward's transposed copies run on this second stream,
+    # beside the attention step (default priority, like every stream here).
+    side = q3.Exec(side_stream=torch.cuda.Stream()) if backward else None
+    nf, nb = len(q3.phase_names(False)), len(q3.phase_names(True))
 
-    def step():
-        q3.layer_forward(lc, W, x, out=out, saved=saved, workspace=fwd_ws, stream=stream)
+    def marks(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+
+    def step(exf=side, exb=None):
+        q3.layer_forward(lc, W, x, out=out, saved=saved, workspace=fwd_ws, stream=stream,
+                         exec=exf)
         if backward:
             q3.layer_backward(lc, W, x, dy, saved, dx=dx, grads=grads,
-                              workspace=ws, stream=stream)
+                              workspace=ws, stream=stream, exec=exb)
 
     for _ in range(warmup):
         step()
@@ -121,9 +178,26 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    k_ms = time_dominant(lc, W["gate"], W["up"], stream, max(10, steps), between=step)
+    # The same steps again with phase marks (events the library records at
+    # its phase boundaries on the stream): per-phase times inside a step.
+    fwd_t, bwd_t = [], []
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        exf = q3.Exec(side_stream=side.side_stream if side else None, marks=marks(nf))
+        exb = q3.Exec(marks=marks(nb)) if backward else None
+        step(exf, exb)
+        fwd_t.append(exf)
+        bwd_t.append(exb)
+    torch.cuda.synchronize()
+    marked_elapsed = time.perf_counter() - t1
+    fwd_ms = np.median(np.array([e.phase_times() for e in fwd_t]), axis=0)
+    bwd_ms = (np.median(np.array([e.phase_times() for e in bwd_t]), axis=0)
+              if backward else None)
     del saved, fwd_ws
-    return {"elapsed": elapsed, "kernel_ms": k_ms}
+    return {"elapsed": elapsed, "marked_elapsed": marked_elapsed,
+            "fwd_phase_ms": dict(zip(q3.phase_names(False), fwd_ms)),
+            "bwd_phase_ms": (dict(zip(q3.phase_names(True), bwd_ms))
+                             if backward else {})}
 
 
 def dominant_operands(lc, gate, up):
@@ -272,8 +346,24 @@ def main():
     T = cfg["B"] * cfg["L"]
     ms = res["elapsed"] / args.steps * 1e3
     tflops = fl["total"] / (ms * 1e-3) / 1e12
+    fwd_work, bwd_work = phase_work(cfg)
+    phases = []
+    for times, work in ((res["fwd_phase_ms"], fwd_work), (res["bwd_phase_ms"], bwd_work)):
+        for name, t in times.items():
+            bound, amount = work[name]
+            if amount == 0 or t <= 0:
+                continue
+            if bound == "mfma":
+                ach, peak, unit = amount / (t * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+            else:
+                ach, peak, unit = amount / (t * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+            phases.append({"phase": name, "ms": round(float(t), 4), "bound": bound,
+                           "work": int(amount), "achieved": round(float(ach), 1),
+                           "unit": unit, "frac": round(float(ach / peak), 4)})
+    dom = "F8-F9 gate/up gemm + swiglu"
+    k_ms = float(res["fwd_phase_ms"][dom])
     k_flops, k_bytes = dominant_work(T, cfg["d"], cfg["d_ffn"])
-    k_tflops = k_flops / (res["kernel_ms"] * 1e-3) / 1e12
+    k_tflops = k_flops / (k_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -301,9 +391,13 @@ def main():
                      "bound": "mfma", "achieved": k_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": k_tflops / PEAK_BF16_TFLOPS,
-                     "avg_ms": res["kernel_ms"],
+                     "avg_ms": k_ms,
+                     "timing": "median over the steps of the launch inside the step, "
+                               "between HIP events the library records on its stream",
                      "algorithmic_bytes": k_bytes,
                      "traffic": traffic_bytes()},
+        "phases": phases,
+        "marked_ms_per_step": res["marked_elapsed"] / args.steps * 1e3,
     }
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)

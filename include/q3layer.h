@@ -1,6 +1,7 @@
 /*
  * q3layer.h -- C ABI of an MI355X (gfx950) implementation of the local
- * compute of one Qwen3 decoder layer, forward and backward.
+ * compute of one Qwen3 decoder layer, forward and backward, plus the ends of
+ * the model around a stack of such layers.
  *
  * What is computed is the layer of the "FSDP2 Qwen3 Decoder Layer
  * Walkthrough" page, section "Decoder Layer 的结构" and forward Steps 1-10:
@@ -15,15 +16,16 @@
  *   y = h + W_down(silu(hn W_gate^T) * hn W_up^T),  hn = RMSNorm(h; w_post)
  *                                                   (Steps 8-10)
  *
- * and its backward ("each operator's backward in reverse order, locally",
- * backward table of the same page): dx and one gradient per parameter.
+ * and its backward (the same page's backward table: the operators' adjoints
+ * run locally, last operator first): dx and one gradient per parameter.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor arguments are DEVICE pointers to caller-owned memory; the
- *    library never allocates device memory, never synchronises, and keeps no
- *    pointer after a call returns.  Work is enqueued on `stream`, a
- *    hipStream_t passed as void* (NULL = the null stream).
+ *    library never allocates device memory, never synchronises, holds no
+ *    mutable global state and keeps no pointer after a call returns.  Work is
+ *    enqueued on `stream`, a hipStream_t passed as void* (NULL = the null
+ *    stream).  Calls on distinct buffers may run from several host threads.
  *  - Layouts are dense row-major.  Activations are [B, L, features] = [T, .]
  *    with T = B * L tokens.  Projection weights are [out, in] (nn.Linear
  *    without bias).  Head j of a projection output occupies features
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define Q3L_VERSION 2
+#define Q3L_VERSION 3
 
 typedef enum { Q3L_F32 = 0, Q3L_BF16 = 1 } q3l_dtype;
 
@@ -123,16 +125,46 @@ typedef struct {
   size_t gu;       /* [T, 2*d_ffn] dtype: gate in columns [0, d_ffn), up in
                       [d_ffn, 2*d_ffn)                                     */
   size_t f;        /* [T, d_ffn] dtype, silu(gate) * up                    */
-  size_t wt;       /* bf16 only (empty for fp32): the projection weights
-                      transposed to [in, out] for the backward's input-
-                      gradient GEMMs: W_down^T [d_ffn, d], then [W_gate;
-                      W_up]^T [d, 2*d_ffn], W_o^T [q_d, d], [W_q; W_k;
-                      W_v]^T [d, q_d + 2*kv_d] (q_d = h_q*d_h, kv_d =
-                      h_kv*d_h), each 256-byte aligned                    */
-  size_t xnt;      /* bf16 only (empty for fp32): xn^T [d, T8] with T8 = T
-                      rounded up to a multiple of 8, columns >= T zero     */
+  size_t wt;       /* bf16 with tp_partial == 0 only (else empty): the
+                      projection weights transposed to [in, out] for the
+                      backward's input-gradient GEMMs: W_down^T [d_ffn, d],
+                      then [W_gate; W_up]^T [d, 2*d_ffn], W_o^T [q_d, d],
+                      [W_q; W_k; W_v]^T [d, q_d + 2*kv_d] (q_d = h_q*d_h,
+                      kv_d = h_kv*d_h), each 256-byte aligned              */
+  size_t xnt;      /* as wt (else empty): xn^T [d, T8] with T8 = T rounded
+                      up to a multiple of 8, columns >= T zero             */
   size_t total;    /* bytes of the whole buffer                            */
 } q3l_saved_layout;
+
+/* Execution options of q3l_layer_forward / q3l_layer_backward.  Pass NULL
+ * for the defaults: every kernel on `stream` and no phase marks.  Every
+ * object named here is created and owned by the caller. */
+typedef struct {
+  /* Optional second stream for work that depends only on the call's inputs:
+   * the bf16 training forward's transposed copies (saved wt and xnt), which
+   * then run beside the attention step.  NULL: they run on `stream`.  When
+   * set, fork_event and join_event must be hipEvent_t the caller created
+   * (timing may be disabled).  The call records fork_event on `stream`,
+   * makes side_stream wait for it, enqueues the copies on side_stream,
+   * records join_event there and makes `stream` wait for it: all work of the
+   * call stays ordered on `stream` (and can be captured into a HIP graph).
+   * Calls that share these objects must not be made concurrently. */
+  void *side_stream;
+  void *fork_event;
+  void *join_event;
+  /* Optional phase marks: NULL, or q3l_phase_count(pass) + 1 hipEvent_t
+   * created by the caller with timing enabled.  marks[0] is recorded on
+   * `stream` before the first kernel of the call and marks[i + 1] after
+   * phase i (phases a call skips are empty), so the elapsed time between
+   * marks[i] and marks[i + 1] is phase i's time on the stream. */
+  void *const *marks;
+  int32_t n_marks;
+} q3l_exec;
+
+/* Number of phases of a forward (backward == 0) or backward (1) call, and
+ * the name of phase i ("F5 attention", ...; NULL out of range). */
+int q3l_phase_count(int backward);
+const char *q3l_phase_name(int backward, int i);
 
 /* Checks a configuration.  Q3L_OK, Q3L_EINVAL or Q3L_EUNSUPPORTED. */
 q3l_status q3l_validate(const q3l_layer_cfg *cfg);
@@ -157,27 +189,40 @@ size_t q3l_workspace_bytes(const q3l_layer_cfg *cfg, int backward);
  *             outlive that call, and x and the weights must not change in
  *             between.
  *   workspace q3l_workspace_bytes(cfg, 0) bytes of scratch (contents
- *             undefined afterwards); workspace_bytes is its size.
- * With bf16 and `saved`, the transposed copies (wt, xnt above) are written
- * by a second stream the library owns (one per device, created on first
- * use, default priority), forked from `stream` with an event before the
- * attention step and joined back into `stream` after it: all work of the
- * call is still ordered on `stream`, and the pattern can be captured into a
- * HIP graph. */
+ *             undefined afterwards); workspace_bytes is its size.  Only
+ *             needed (and only checked) when saved is NULL.
+ *   exec      NULL or execution options (see q3l_exec). */
 q3l_status q3l_layer_forward(const q3l_layer_cfg *cfg, const q3l_weights *w,
                              const void *x, const q3l_outputs *out,
                              void *saved, void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             size_t workspace_bytes, void *stream,
+                             const q3l_exec *exec);
 
 /* Backward flags.  INPUT: compute dx.  WEIGHT: compute the eleven weight
  * gradients.  ACCUMULATE: add weight gradients into the buffers instead of
- * overwriting them (gradient accumulation across micro-batches). */
-enum { Q3L_BWD_INPUT = 1, Q3L_BWD_WEIGHT = 2, Q3L_BWD_ACCUMULATE = 4 };
+ * overwriting them (gradient accumulation across micro-batches).
+ * DEFERRED_WEIGHT (with WEIGHT, without INPUT): the input-gradient half of
+ * the backward was already run by an INPUT-only call on the same workspace
+ * (same cfg, weights, x, dy and saved), which leaves the activation
+ * gradients and the norm-weight partial sums there; only the weight-
+ * gradient GEMMs (with their operand transposes) and the norm-weight
+ * reductions run.  This is the split of the backward into an input-gradient
+ * part B and a weight-gradient part W of the parallelism page's pipeline
+ * section (zero-bubble schedules): INPUT then WEIGHT|DEFERRED_WEIGHT gives
+ * bitwise the results of one INPUT|WEIGHT call. */
+enum {
+  Q3L_BWD_INPUT = 1,
+  Q3L_BWD_WEIGHT = 2,
+  Q3L_BWD_ACCUMULATE = 4,
+  Q3L_BWD_DEFERRED_WEIGHT = 8
+};
 
 /* Backward of the layer given dy = dLoss/dy [T, d] (cfg.dtype).
- *   saved  the buffer a forward with the same cfg, weights and x filled.
- *   dx     [T, d] cfg.dtype (written when flags & Q3L_BWD_INPUT).
- *   grads  fp32 gradient buffers (written when flags & Q3L_BWD_WEIGHT).
+ *   saved     the buffer a forward with the same cfg, weights and x filled.
+ *   dx        [T, d] cfg.dtype (written when flags & Q3L_BWD_INPUT).
+ *   grads     fp32 gradient buffers (written when flags & Q3L_BWD_WEIGHT).
+ *   workspace q3l_workspace_bytes(cfg, 1) bytes; between an INPUT-only call
+ *             and its DEFERRED_WEIGHT call it must not be reused.
  *   Attention probabilities are recomputed from the saved log-sum-exp.
  *   Not available for tp_partial layers (Q3L_EUNSUPPORTED). */
 q3l_status q3l_layer_backward(const q3l_layer_cfg *cfg, const q3l_weights *w,
@@ -185,7 +230,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg *cfg, const q3l_weights *w,
                               const void *saved, void *dx,
                               const q3l_grads *grads, int flags,
                               void *workspace, size_t workspace_bytes,
-                              void *stream);
+                              void *stream, const q3l_exec *exec);
 
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char *q3l_last_error(void);
@@ -206,9 +251,72 @@ q3l_status q3l_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t n,
                            const void *x, const void *w, float eps, void *y,
                            float *rstd, void *stream);
 
+/* Adjoint of q3l_rmsnorm_fwd (walkthrough page, backward of Steps 1 and 8),
+ * given the forward's x and rstd:
+ *   dx[r, :] = rstd (g - xhat mean(g xhat)) + resid[r, :],
+ *   with xhat = x rstd and g = dy w;   dw (+)= sum_r dy[r, :] xhat[r, :].
+ * dy, x, resid (optional, may be NULL), dx: [rows, n] dtype; w [n] dtype;
+ * dw [n] fp32 (optional: NULL computes dx only), overwritten, or added into
+ * when accumulate != 0; the sum over rows has a fixed order.  workspace:
+ * q3l_rmsnorm_bwd_workspace_bytes(n) bytes of scratch (partial sums of dw).
+ * n as for q3l_rmsnorm_fwd. */
+size_t q3l_rmsnorm_bwd_workspace_bytes(int32_t n);
+q3l_status q3l_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t n,
+                           const void *dy, const void *x, const float *rstd,
+                           const void *w, const void *resid, void *dx,
+                           float *dw, int accumulate, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* RoPE angle table (walkthrough page, Step 4): for position t < L and pair
+ * i < d_h/2, angle t * theta^(-2i/d_h) (computed in double), cos_t[t, i] and
+ * sin_t[t, i] fp32 [L, d_h/2].  The pairing is rotate-half: element i of a
+ * head vector pairs with element i + d_h/2. */
+q3l_status q3l_rope_table(int32_t L, int32_t d_h, float theta, float *cos_t,
+                          float *sin_t, void *stream);
+
+/* Steps 3-4 of the walkthrough page in one pass: for every token t (position
+ * t % L) and every head of a [B*L, ld_in] buffer whose columns hold h_q
+ * query heads then h_kv key heads of d_h each, the per-head RMSNorm over d_h
+ * with weight wq (query heads) or wk (key heads) -- skipped when
+ * qk_norm == 0 -- then the rotation by the angles of q3l_rope_table:
+ *   out[i] = n[i] cos - n[i + d_h/2] sin,  out[i + d_h/2] = n[i + d_h/2] cos
+ *   + n[i] sin   (i < d_h/2).
+ * out has the same column arrangement with row stride ld_out; rstd_q
+ * [B*L, h_q] and rstd_k [B*L, h_kv] fp32 receive the norms' reciprocal
+ * rms (unused when qk_norm == 0). */
+q3l_status q3l_qknorm_rope_fwd(int32_t dtype, int32_t B, int32_t L,
+                               int32_t h_q, int32_t h_kv, int32_t d_h,
+                               int32_t qk_norm, float eps, const void *in,
+                               int64_t ld_in, const void *wq, const void *wk,
+                               const float *cos_t, const float *sin_t,
+                               void *out, int64_t ld_out, float *rstd_q,
+                               float *rstd_k, void *stream);
+
+/* Adjoint of q3l_qknorm_rope_fwd: g (gradient w.r.t. its output, stride
+ * ld_g) is rotated back (the rotation by the opposite angle), then taken
+ * through the per-head RMSNorm given the forward's input `pre` (stride
+ * ld_pre) and rstd_q / rstd_k; out (stride ld_out) receives the gradient
+ * w.r.t. the forward's input.  dwq, dwk [d_h] fp32 (overwritten, or added
+ * into when accumulate != 0; NULL skips) receive the norm weights'
+ * gradients summed over tokens and heads in a fixed order.  workspace:
+ * q3l_qknorm_rope_bwd_workspace_bytes(d_h) bytes of scratch. */
+size_t q3l_qknorm_rope_bwd_workspace_bytes(int32_t d_h);
+q3l_status q3l_qknorm_rope_bwd(int32_t dtype, int32_t B, int32_t L,
+                               int32_t h_q, int32_t h_kv, int32_t d_h,
+                               int32_t qk_norm, const void *g, int64_t ld_g,
+                               const void *pre, int64_t ld_pre,
+                               const void *wq, const void *wk,
+                               const float *rstd_q, const float *rstd_k,
+                               const float *cos_t, const float *sin_t,
+                               void *out, int64_t ld_out, float *dwq,
+                               float *dwk, int accumulate, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* y[M, N] = a[M, K] * w[N, K]^T (+ resid[M, N] if resid != NULL), the
  * bias-free linear layer of Steps 2, 6 and 9.  dtype elements; y and resid
- * may not alias a or w. */
+ * may not alias a or w.  bf16: (M + 8) * max(N, K) * 2 and (N + 8) * K * 2
+ * bytes must stay below 2^31 (Q3L_EUNSUPPORTED beyond; the same holds for
+ * the dgrad, wgrad and SwiGLU calls below). */
 q3l_status q3l_linear_fwd(int32_t dtype, int64_t M, int32_t N, int32_t K,
                           const void *a, const void *w, const void *resid,
                           void *y, void *stream);
@@ -234,31 +342,43 @@ q3l_status q3l_swiglu_fwd(int32_t dtype, int64_t M, int32_t N, int32_t K,
                           const void *hn, const void *gate, const void *up,
                           void *f, void *gu, void *stream);
 
+/* Adjoint of f = silu(g) * u (walkthrough page, Step 9), with s = sigmoid(g):
+ *   dg = df u s (1 + g (1 - s)),  du = df g s.
+ * df [M, N]; gu [M, 2N] holds g in columns [0, N) and u in [N, 2N); dgu
+ * [M, 2N] receives dg then du (dtype; N a multiple of 8).  dgu may not
+ * alias gu; it may alias df only when df is dgu's dg half (row stride 2N,
+ * which this call does not take: pass distinct buffers). */
+q3l_status q3l_swiglu_bwd(int32_t dtype, int64_t M, int32_t N, const void *df,
+                          const void *gu, void *dgu, void *stream);
+
 /* Causal GQA attention (walkthrough page, Step 5) on one batch:
  *   q [B*L, h_q*d_h] with row stride ldq, k/v [B*L, h_kv*d_h] with row
  *   strides ldk/ldv, o [B*L, h_q*d_h] with row stride ldo (dtype);
  *   lse [B, h_q, L] fp32 (natural log).  Scale 1/sqrt(d_h).
  *   bf16: (B*L + 64) * max(ldq, ldk, ldv, ldo) * 2 and B*L*h_q*4 must stay
  *   below 2^31 (Q3L_EUNSUPPORTED otherwise; the same bound holds for
- *   q3l_attention_bwd). */
+ *   q3l_attention_bwd with its strides). */
 q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L,
                              int32_t h_q, int32_t h_kv, int32_t d_h,
                              const void *q, int64_t ldq, const void *k,
                              int64_t ldk, const void *v, int64_t ldv, void *o,
                              int64_t ldo, float *lse, void *stream);
 
-/* Its backward: dq, dk, dv (dtype, same layouts/strides as q, k, v) from
- * dout (stride ldo like o), o, lse.  P is recomputed from lse.
- * workspace: q3l_attention_bwd_workspace_bytes(B, L, h_q) bytes. */
+/* Its backward: dq, dk, dv (dtype) are written with the row strides of q, k,
+ * v (ldq, ldk, ldv) -- a caller that passes strided views must give dq, dk,
+ * dv buffers of the same strides -- from o (stride ldo), dout (stride
+ * lddo) and lse.  P is recomputed from lse.  workspace:
+ * q3l_attention_bwd_workspace_bytes(B, L, h_q) bytes of scratch (the row
+ * sums of dout * o). */
 size_t q3l_attention_bwd_workspace_bytes(int32_t B, int32_t L, int32_t h_q);
 q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L,
                              int32_t h_q, int32_t h_kv, int32_t d_h,
                              const void *q, int64_t ldq, const void *k,
                              int64_t ldk, const void *v, int64_t ldv,
-                             const void *o, const void *dout, int64_t ldo,
-                             const float *lse, void *dq, void *dk, void *dv,
-                             void *workspace, size_t workspace_bytes,
-                             void *stream);
+                             const void *o, int64_t ldo, const void *dout,
+                             int64_t lddo, const float *lse, void *dq,
+                             void *dk, void *dv, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

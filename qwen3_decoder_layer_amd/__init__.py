@@ -3,8 +3,9 @@ backward) on an MI355X, computed entirely by the library's HIP kernels.
 
 The functions below have the names of the C ABI in include/q3layer.h minus
 the ``q3l_`` prefix.  They only marshal arguments: tensors are torch tensors
-on the GPU (PyTorch supplies device memory and the current stream), and any
-buffer the caller does not pass is allocated with ``torch.empty``.  If the
+on the GPU (PyTorch supplies device memory, streams and events), and any
+buffer the caller does not pass is allocated with ``torch.empty``.  Shapes,
+dtypes and sizes are checked here before a pointer crosses the C ABI.  If the
 library is missing the calls raise; there is no fallback path.
 """
 from __future__ import annotations
@@ -13,13 +14,16 @@ import ctypes as C
 from dataclasses import dataclass, asdict
 
 from . import _abi
-from ._abi import BWD_ACCUMULATE, BWD_INPUT, BWD_WEIGHT, PARAMS, Q3L_BF16, Q3L_F32
+from ._abi import (BWD_ACCUMULATE, BWD_DEFERRED_WEIGHT, BWD_INPUT, BWD_WEIGHT,
+                   PARAMS, Q3L_BF16, Q3L_F32)
 
-__all__ = ["LayerConfig", "Q3LError", "validate", "saved_bytes",
-           "workspace_bytes", "saved_layout", "layer_forward",
-           "layer_backward", "rmsnorm_fwd", "linear_fwd", "linear_dgrad",
-           "linear_wgrad", "swiglu_fwd", "attention_fwd", "attention_bwd", "library",
-           "PARAMS", "BWD_INPUT", "BWD_WEIGHT", "BWD_ACCUMULATE"]
+__all__ = ["LayerConfig", "Q3LError", "Exec", "validate", "saved_bytes",
+           "workspace_bytes", "saved_layout", "phase_names", "layer_forward",
+           "layer_backward", "rmsnorm_fwd", "rmsnorm_bwd", "rope_table",
+           "qknorm_rope_fwd", "qknorm_rope_bwd", "linear_fwd", "linear_dgrad",
+           "linear_wgrad", "swiglu_fwd", "swiglu_bwd", "attention_fwd",
+           "attention_bwd", "library", "param_shapes", "PARAMS", "BWD_INPUT",
+           "BWD_WEIGHT", "BWD_ACCUMULATE", "BWD_DEFERRED_WEIGHT"]
 
 
 class Q3LError(RuntimeError):
@@ -69,6 +73,15 @@ class LayerConfig:
         return asdict(self)
 
 
+def param_shapes(cfg: LayerConfig) -> dict:
+    """Shapes of the eleven parameters as the C ABI reads them."""
+    qd, kvd = cfg.h_q * cfg.d_h, cfg.h_kv * cfg.d_h
+    return {"in_norm": (cfg.d,), "q": (qd, cfg.d), "k": (kvd, cfg.d),
+            "v": (kvd, cfg.d), "q_norm": (cfg.d_h,), "k_norm": (cfg.d_h,),
+            "o": (cfg.d, qd), "post_norm": (cfg.d,), "gate": (cfg.d_ffn, cfg.d),
+            "up": (cfg.d_ffn, cfg.d), "down": (cfg.d, cfg.d_ffn)}
+
+
 def _check(status: int):
     if status != 0:
         msg = library().q3l_last_error().decode()
@@ -95,6 +108,80 @@ def _code(dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 
+def _need(t, name, numel=None, dtype=None, contiguous=True, min_bytes=None):
+    """Raise unless tensor t is on the GPU with the given size and dtype."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                         f"{min_bytes} needed")
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+class Exec:
+    """Execution options of layer_forward / layer_backward (q3l_exec).
+
+    side_stream: a torch.cuda.Stream for the bf16 training forward's
+    transposed copies (run beside the attention step; two events for the
+    fork and join are created here).  marks: a list of
+    ``phase_count + 1`` timing events (``torch.cuda.Event(enable_timing=
+    True)``), recorded by the library at the phase boundaries; read them back
+    with ``phase_times()`` after synchronising."""
+
+    def __init__(self, side_stream=None, marks=None):
+        import torch
+        self.side_stream = side_stream
+        self.marks = list(marks) if marks else None
+        self._fork = self._join = None
+        if side_stream is not None:
+            self._fork, self._join = torch.cuda.Event(), torch.cuda.Event()
+            # torch creates the HIP event on its first record.
+            for e in (self._fork, self._join):
+                e.record(side_stream)
+        if self.marks:
+            for e in self.marks:
+                e.record()
+        self._arr = None
+
+    def c_struct(self) -> _abi.Exec:
+        ex = _abi.Exec()
+        if self.side_stream is not None:
+            ex.side_stream = self.side_stream.cuda_stream
+            ex.fork_event = self._fork.cuda_event
+            ex.join_event = self._join.cuda_event
+        if self.marks:
+            self._arr = (C.c_void_p * len(self.marks))(
+                *[e.cuda_event for e in self.marks])
+            ex.marks = C.cast(self._arr, C.POINTER(C.c_void_p))
+            ex.n_marks = len(self.marks)
+        return ex
+
+    def phase_times(self):
+        """Milliseconds of each phase from the last call's marks."""
+        return [a.elapsed_time(b) for a, b in zip(self.marks, self.marks[1:])]
+
+
+def _exec(ex):
+    return None if ex is None else C.byref(ex.c_struct())
+
+
+def phase_names(backward: bool) -> list:
+    lib = library()
+    b = int(bool(backward))
+    return [lib.q3l_phase_name(b, i).decode() for i in range(lib.q3l_phase_count(b))]
+
+
 def validate(cfg: LayerConfig) -> None:
     c = cfg.c_struct()
     _check(library().q3l_validate(C.byref(c)))
@@ -117,7 +204,13 @@ def saved_layout(cfg: LayerConfig) -> dict:
     return {n: getattr(lay, n) for n in _abi.SAVED_FIELDS}
 
 
-def _weights(w: dict) -> _abi.Weights:
+def _weights(cfg: LayerConfig, w: dict) -> _abi.Weights:
+    shapes = param_shapes(cfg)
+    for n in PARAMS:
+        if not cfg.qk_norm and n in ("q_norm", "k_norm") and w.get(n) is None:
+            continue
+        _need(w.get(n), f"weights[{n!r}]", numel=int(__import__("math").prod(shapes[n])),
+              dtype=cfg.torch_dtype)
     return _abi.Weights(*[None if w.get(n) is None else w[n].data_ptr()
                           for n in PARAMS])
 
@@ -128,87 +221,193 @@ def _bytes(n, device):
 
 
 def layer_forward(cfg: LayerConfig, weights: dict, x, out: dict | None = None,
-                  saved=None, workspace=None, stream=None) -> dict:
+                  saved=None, workspace=None, stream=None, exec=None) -> dict:
     """q3l_layer_forward.  x: [B, L, d] (or [T, d]) tensor of cfg's dtype.
 
     Returns {"y"} or, for tp_partial, {"attn_partial", "mlp_partial"}
     (fp32).  Pass ``saved`` (uint8, ``saved_bytes(cfg)``) to keep the
-    intermediates for ``layer_backward``."""
+    intermediates for ``layer_backward``; ``exec`` is an optional Exec."""
     import torch
     c = cfg.c_struct()
     lib = library()
+    _need(x, "x", numel=cfg.T * cfg.d, dtype=cfg.torch_dtype)
     out = dict(out or {})
     shape = (cfg.B, cfg.L, cfg.d)
     if cfg.tp_partial:
         for k in ("attn_partial", "mlp_partial"):
             if out.get(k) is None:
                 out[k] = torch.empty(shape, dtype=torch.float32, device=x.device)
+            _need(out[k], k, numel=cfg.T * cfg.d, dtype=torch.float32)
         o = _abi.Outputs(None, out["attn_partial"].data_ptr(),
                          out["mlp_partial"].data_ptr())
     else:
         if out.get("y") is None:
             out["y"] = torch.empty(shape, dtype=x.dtype, device=x.device)
+        _need(out["y"], "y", numel=cfg.T * cfg.d, dtype=cfg.torch_dtype)
         o = _abi.Outputs(out["y"].data_ptr(), None, None)
-    ws_n = 0
-    if saved is None and workspace is None:
+    if saved is not None:
+        _need(saved, "saved", min_bytes=saved_bytes(cfg))
+    elif workspace is None:
         workspace = _bytes(workspace_bytes(cfg, False), x.device)
     if workspace is not None:
-        ws_n = workspace.numel() * workspace.element_size()
-    w = _weights(weights)
+        _need(workspace, "workspace")
+    w = _weights(cfg, weights)
     _check(lib.q3l_layer_forward(C.byref(c), C.byref(w), _p(x), C.byref(o),
-                                 _p(saved), _p(workspace), ws_n,
-                                 _stream(stream)))
+                                 _p(saved), _p(workspace), _nbytes(workspace),
+                                 _stream(stream), _exec(exec)))
     return out
 
 
 def layer_backward(cfg: LayerConfig, weights: dict, x, dy, saved, dx=None,
                    grads: dict | None = None,
                    flags: int = BWD_INPUT | BWD_WEIGHT, workspace=None,
-                   stream=None):
+                   stream=None, exec=None):
     """q3l_layer_backward.  Returns (dx, grads) with grads a dict of fp32
-    tensors shaped like the parameters."""
+    tensors shaped like the parameters.  For a split backward, pass the
+    same ``workspace`` to the INPUT call and to its WEIGHT |
+    DEFERRED_WEIGHT call."""
     import torch
     c = cfg.c_struct()
     lib = library()
+    td = cfg.torch_dtype
+    _need(x, "x", numel=cfg.T * cfg.d, dtype=td)
+    _need(dy, "dy", numel=cfg.T * cfg.d, dtype=td)
+    _need(saved, "saved", min_bytes=saved_bytes(cfg))
     if (flags & BWD_INPUT) and dx is None:
         dx = torch.empty_like(x)
+    if dx is not None:
+        _need(dx, "dx", numel=cfg.T * cfg.d, dtype=td)
     if flags & BWD_WEIGHT:
         grads = dict(grads or {})
-        for n in PARAMS:
+        for n, shp in param_shapes(cfg).items():
             if grads.get(n) is None:
-                grads[n] = torch.empty(weights[n].shape, dtype=torch.float32,
-                                       device=x.device)
+                grads[n] = torch.empty(shp, dtype=torch.float32, device=x.device)
+            _need(grads[n], f"grads[{n!r}]", numel=int(__import__("math").prod(shp)),
+                  dtype=torch.float32)
     g = _abi.Grads(*[None if not grads or grads.get(n) is None
                      else grads[n].data_ptr() for n in PARAMS])
     if workspace is None:
         workspace = _bytes(workspace_bytes(cfg, True), x.device)
-    ws_n = workspace.numel() * workspace.element_size()
-    w = _weights(weights)
+    _need(workspace, "workspace")
+    w = _weights(cfg, weights)
     _check(lib.q3l_layer_backward(C.byref(c), C.byref(w), _p(x), _p(dy),
                                   _p(saved), _p(dx), C.byref(g), flags,
-                                  _p(workspace), ws_n, _stream(stream)))
+                                  _p(workspace), _nbytes(workspace),
+                                  _stream(stream), _exec(exec)))
     return dx, grads
 
 
 # ---- phase-level calls --------------------------------------------------
+def _rows_n(x):
+    return x.numel() // x.shape[-1], x.shape[-1]
+
+
 def rmsnorm_fwd(x, w, eps, y=None, rstd=None, stream=None):
     import torch
-    rows = x.numel() // x.shape[-1]
+    rows, n = _rows_n(x)
+    _need(x, "x")
+    _need(w, "w", numel=n, dtype=x.dtype)
     y = torch.empty_like(x) if y is None else y
     rstd = (torch.empty(rows, dtype=torch.float32, device=x.device)
             if rstd is None else rstd)
-    _check(library().q3l_rmsnorm_fwd(_code(x.dtype), rows, x.shape[-1], _p(x),
-                                     _p(w), eps, _p(y), _p(rstd),
-                                     _stream(stream)))
+    _need(y, "y", numel=x.numel(), dtype=x.dtype)
+    _need(rstd, "rstd", numel=rows, dtype=torch.float32)
+    _check(library().q3l_rmsnorm_fwd(_code(x.dtype), rows, n, _p(x), _p(w), eps,
+                                     _p(y), _p(rstd), _stream(stream)))
     return y, rstd
+
+
+def rmsnorm_bwd(dy, x, rstd, w, resid=None, dx=None, dw=None, accumulate=False,
+                want_dw=True, workspace=None, stream=None):
+    """dx = resid + RMSNorm adjoint; dw (+)= sum over rows (fp32)."""
+    import torch
+    rows, n = _rows_n(x)
+    for t, name in ((dy, "dy"), (x, "x")):
+        _need(t, name, numel=rows * n, dtype=x.dtype)
+    _need(rstd, "rstd", numel=rows, dtype=torch.float32)
+    _need(w, "w", numel=n, dtype=x.dtype)
+    if resid is not None:
+        _need(resid, "resid", numel=rows * n, dtype=x.dtype)
+    dx = torch.empty_like(x) if dx is None else dx
+    _need(dx, "dx", numel=rows * n, dtype=x.dtype)
+    if want_dw and dw is None:
+        dw = torch.empty(n, dtype=torch.float32, device=x.device)
+    if dw is not None:
+        _need(dw, "dw", numel=n, dtype=torch.float32)
+    lib = library()
+    nb = lib.q3l_rmsnorm_bwd_workspace_bytes(n)
+    workspace = _bytes(nb, x.device) if workspace is None else workspace
+    _check(lib.q3l_rmsnorm_bwd(_code(x.dtype), rows, n, _p(dy), _p(x), _p(rstd),
+                               _p(w), _p(resid), _p(dx), _p(dw), int(bool(accumulate)),
+                               _p(workspace), _nbytes(workspace), _stream(stream)))
+    return dx, dw
+
+
+def rope_table(L, d_h, theta, device="cuda", stream=None):
+    """(cos, sin), each fp32 [L, d_h/2]."""
+    import torch
+    cos = torch.empty((L, d_h // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check(library().q3l_rope_table(L, d_h, theta, _p(cos), _p(sin), _stream(stream)))
+    return cos, sin
+
+
+def qknorm_rope_fwd(qk, wq, wk, cos, sin, h_q, h_kv, d_h, eps=1e-6, qk_norm=True,
+                    out=None, rstd_q=None, rstd_k=None, stream=None):
+    """qk: [B, L, >= (h_q + h_kv) d_h] with h_q query heads then h_kv key
+    heads (row stride from the tensor).  Returns (out, rstd_q, rstd_k)."""
+    import torch
+    B, L = qk.shape[0], qk.shape[1]
+    w = (h_q + h_kv) * d_h
+    out = torch.empty((B, L, w), dtype=qk.dtype, device=qk.device) if out is None else out
+    rstd_q = (torch.empty((B * L, h_q), dtype=torch.float32, device=qk.device)
+              if rstd_q is None else rstd_q)
+    rstd_k = (torch.empty((B * L, h_kv), dtype=torch.float32, device=qk.device)
+              if rstd_k is None else rstd_k)
+    for t, name in ((cos, "cos"), (sin, "sin")):
+        _need(t, name, numel=L * d_h // 2, dtype=torch.float32)
+    _need(rstd_q, "rstd_q", numel=B * L * h_q, dtype=torch.float32)
+    _need(rstd_k, "rstd_k", numel=B * L * h_kv, dtype=torch.float32)
+    _check(library().q3l_qknorm_rope_fwd(
+        _code(qk.dtype), B, L, h_q, h_kv, d_h, int(bool(qk_norm)), eps, _p(qk),
+        qk.stride(1), _p(wq), _p(wk), _p(cos), _p(sin), _p(out), out.stride(1),
+        _p(rstd_q), _p(rstd_k), _stream(stream)))
+    return out, rstd_q, rstd_k
+
+
+def qknorm_rope_bwd(g, pre, wq, wk, rstd_q, rstd_k, cos, sin, h_q, h_kv, d_h,
+                    qk_norm=True, out=None, dwq=None, dwk=None, accumulate=False,
+                    stream=None):
+    """Adjoint of qknorm_rope_fwd.  Returns (out, dwq, dwk)."""
+    import torch
+    B, L = g.shape[0], g.shape[1]
+    w = (h_q + h_kv) * d_h
+    out = torch.empty((B, L, w), dtype=g.dtype, device=g.device) if out is None else out
+    if qk_norm:
+        dwq = torch.empty(d_h, dtype=torch.float32, device=g.device) if dwq is None else dwq
+        dwk = torch.empty(d_h, dtype=torch.float32, device=g.device) if dwk is None else dwk
+    lib = library()
+    nb = lib.q3l_qknorm_rope_bwd_workspace_bytes(d_h)
+    ws = _bytes(nb, g.device)
+    _check(lib.q3l_qknorm_rope_bwd(
+        _code(g.dtype), B, L, h_q, h_kv, d_h, int(bool(qk_norm)), _p(g), g.stride(1),
+        _p(pre), 0 if pre is None else pre.stride(1), _p(wq), _p(wk), _p(rstd_q),
+        _p(rstd_k), _p(cos), _p(sin), _p(out), out.stride(1), _p(dwq), _p(dwk),
+        int(bool(accumulate)), _p(ws), nb, _stream(stream)))
+    return out, dwq, dwk
 
 
 def linear_fwd(a, w, resid=None, y=None, stream=None):
     import torch
-    M, K = a.numel() // a.shape[-1], a.shape[-1]
+    M, K = _rows_n(a)
     N = w.shape[0]
+    _need(a, "a")
+    _need(w, "w", numel=N * K, dtype=a.dtype)
     y = torch.empty((*a.shape[:-1], N), dtype=a.dtype, device=a.device) \
         if y is None else y
+    _need(y, "y", numel=M * N, dtype=a.dtype)
+    if resid is not None:
+        _need(resid, "resid", numel=M * N, dtype=a.dtype)
     _check(library().q3l_linear_fwd(_code(a.dtype), M, N, K, _p(a), _p(w),
                                     _p(resid), _p(y), _stream(stream)))
     return y
@@ -216,10 +415,13 @@ def linear_fwd(a, w, resid=None, y=None, stream=None):
 
 def linear_dgrad(dy, w, da=None, stream=None):
     import torch
-    M, N = dy.numel() // dy.shape[-1], dy.shape[-1]
+    M, N = _rows_n(dy)
     K = w.shape[1]
+    _need(dy, "dy")
+    _need(w, "w", numel=N * K, dtype=dy.dtype)
     da = torch.empty((*dy.shape[:-1], K), dtype=dy.dtype, device=dy.device) \
         if da is None else da
+    _need(da, "da", numel=M * K, dtype=dy.dtype)
     _check(library().q3l_linear_dgrad(_code(dy.dtype), M, N, K, _p(dy), _p(w),
                                       _p(da), _stream(stream)))
     return da
@@ -227,9 +429,13 @@ def linear_dgrad(dy, w, da=None, stream=None):
 
 def linear_wgrad(dy, a, dw=None, accumulate=False, stream=None):
     import torch
-    M, N, K = dy.numel() // dy.shape[-1], dy.shape[-1], a.shape[-1]
+    M, N = _rows_n(dy)
+    K = a.shape[-1]
+    _need(dy, "dy")
+    _need(a, "a", numel=M * K, dtype=dy.dtype)
     dw = torch.empty((N, K), dtype=torch.float32, device=dy.device) \
         if dw is None else dw
+    _need(dw, "dw", numel=N * K, dtype=torch.float32)
     _check(library().q3l_linear_wgrad(_code(dy.dtype), M, N, K, _p(dy), _p(a),
                                       _p(dw), int(bool(accumulate)),
                                       _stream(stream)))
@@ -240,13 +446,34 @@ def swiglu_fwd(hn, gate, up, f=None, gu=None, stream=None):
     """f = silu(hn gate^T) * (hn up^T) with the layer's fused kernel; gu
     (optional [M, 2N]) receives gate | up pre-activations."""
     import torch
-    M, K, N = hn.numel() // hn.shape[-1], hn.shape[-1], gate.shape[0]
+    M, K = _rows_n(hn)
+    N = gate.shape[0]
+    _need(hn, "hn")
+    _need(gate, "gate", numel=N * K, dtype=hn.dtype)
+    _need(up, "up", numel=N * K, dtype=hn.dtype)
     f = torch.empty((*hn.shape[:-1], N), dtype=hn.dtype, device=hn.device) \
         if f is None else f
+    _need(f, "f", numel=M * N, dtype=hn.dtype)
+    if gu is not None:
+        _need(gu, "gu", numel=M * 2 * N, dtype=hn.dtype)
     _check(library().q3l_swiglu_fwd(_code(hn.dtype), M, N, K, _p(hn),
                                     _p(gate), _p(up), _p(f), _p(gu),
                                     _stream(stream)))
     return f
+
+
+def swiglu_bwd(df, gu, dgu=None, stream=None):
+    """dg | du ([M, 2N]) from df [M, N] and g | u [M, 2N]."""
+    import torch
+    M, N = _rows_n(df)
+    _need(df, "df")
+    _need(gu, "gu", numel=M * 2 * N, dtype=df.dtype)
+    dgu = torch.empty((*df.shape[:-1], 2 * N), dtype=df.dtype, device=df.device) \
+        if dgu is None else dgu
+    _need(dgu, "dgu", numel=M * 2 * N, dtype=df.dtype)
+    _check(library().q3l_swiglu_bwd(_code(df.dtype), M, N, _p(df), _p(gu), _p(dgu),
+                                    _stream(stream)))
+    return dgu
 
 
 def attention_fwd(q, k, v, h_q, h_kv, d_h, o=None, lse=None, stream=None):
@@ -258,6 +485,7 @@ def attention_fwd(q, k, v, h_q, h_kv, d_h, o=None, lse=None, stream=None):
         if o is None else o
     lse = torch.empty((B, h_q, L), dtype=torch.float32, device=q.device) \
         if lse is None else lse
+    _need(lse, "lse", numel=B * h_q * L, dtype=torch.float32)
     _check(library().q3l_attention_fwd(
         _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k),
         k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(lse),
@@ -265,18 +493,30 @@ def attention_fwd(q, k, v, h_q, h_kv, d_h, o=None, lse=None, stream=None):
     return o, lse
 
 
+def _like_strided(t):
+    """An uninitialised tensor with t's sizes and strides (so a strided view
+    gets an output of the layout the library writes)."""
+    import torch
+    return torch.empty_strided(t.size(), t.stride(), dtype=t.dtype, device=t.device)
+
+
 def attention_bwd(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq=None, dk=None,
                   dv=None, stream=None):
-    import torch
+    """dq, dk, dv are written with q, k, v's row strides: by default they
+    are allocated with the same strides."""
     B, L = q.shape[0], q.shape[1]
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _like_strided(q) if dq is None else dq
+    dk = _like_strided(k) if dk is None else dk
+    dv = _like_strided(v) if dv is None else dv
+    for a, b, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if a.stride() != b.stride() or a.shape != b.shape:
+            raise ValueError(f"{name} must have the shape and strides of its input")
     lib = library()
     n = lib.q3l_attention_bwd_workspace_bytes(B, L, h_q)
     ws = _bytes(n, q.device)
     _check(lib.q3l_attention_bwd(
         _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k),
-        k.stride(1), _p(v), v.stride(1), _p(o), _p(dout), dout.stride(1),
-        _p(lse), _p(dq), _p(dk), _p(dv), _p(ws), n, _stream(stream)))
+        k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(dout),
+        dout.stride(1), _p(lse), _p(dq), _p(dk), _p(dv), _p(ws), n,
+        _stream(stream)))
     return dq, dk, dv

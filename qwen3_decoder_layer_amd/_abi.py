@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 Q3L_F32, Q3L_BF16 = 0, 1
 STATUS = {0: "Q3L_OK", 1: "Q3L_EINVAL", 2: "Q3L_EUNSUPPORTED",
           3: "Q3L_EALIGN", 4: "Q3L_EHIP"}
-BWD_INPUT, BWD_WEIGHT, BWD_ACCUMULATE = 1, 2, 4
+BWD_INPUT, BWD_WEIGHT, BWD_ACCUMULATE, BWD_DEFERRED_WEIGHT = 1, 2, 4, 8
 
 PARAMS = ("in_norm", "q", "k", "v", "q_norm", "k_norm", "o", "post_norm",
           "gate", "up", "down")
@@ -50,6 +50,12 @@ class SavedLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in SAVED_FIELDS]
 
 
+class Exec(C.Structure):
+    _fields_ = [("side_stream", C.c_void_p), ("fork_event", C.c_void_p),
+                ("join_event", C.c_void_p), ("marks", C.POINTER(C.c_void_p)),
+                ("n_marks", C.c_int32)]
+
+
 # name -> (restype, argtypes)
 _vp, _i32, _i64, _sz, _f = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
 PROTOTYPES = {
@@ -58,14 +64,30 @@ PROTOTYPES = {
     "q3l_saved_bytes": (_sz, [C.POINTER(Cfg)]),
     "q3l_workspace_bytes": (_sz, [C.POINTER(Cfg), C.c_int]),
     "q3l_layer_forward": (C.c_int, [C.POINTER(Cfg), C.POINTER(Weights), _vp,
-                                    C.POINTER(Outputs), _vp, _vp, _sz, _vp]),
+                                    C.POINTER(Outputs), _vp, _vp, _sz, _vp,
+                                    C.POINTER(Exec)]),
     "q3l_layer_backward": (C.c_int, [C.POINTER(Cfg), C.POINTER(Weights), _vp,
                                      _vp, _vp, _vp, C.POINTER(Grads), C.c_int,
-                                     _vp, _sz, _vp]),
+                                     _vp, _sz, _vp, C.POINTER(Exec)]),
+    "q3l_phase_count": (C.c_int, [C.c_int]),
+    "q3l_phase_name": (C.c_char_p, [C.c_int, C.c_int]),
     "q3l_last_error": (C.c_char_p, []),
     "q3l_version": (C.c_int, []),
     "q3l_rmsnorm_fwd": (C.c_int, [_i32, _i64, _i32, _vp, _vp, _f, _vp, _vp,
                                   _vp]),
+    "q3l_rmsnorm_bwd_workspace_bytes": (_sz, [_i32]),
+    "q3l_rmsnorm_bwd": (C.c_int, [_i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, C.c_int, _vp, _sz, _vp]),
+    "q3l_rope_table": (C.c_int, [_i32, _i32, _f, _vp, _vp, _vp]),
+    "q3l_qknorm_rope_fwd": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _f, _vp, _i64, _vp, _vp, _vp, _vp,
+                                      _vp, _i64, _vp, _vp, _vp]),
+    "q3l_qknorm_rope_bwd_workspace_bytes": (_sz, [_i32]),
+    "q3l_qknorm_rope_bwd": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _vp, _i64, _vp, _i64, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                                      C.c_int, _vp, _sz, _vp]),
+    "q3l_swiglu_bwd": (C.c_int, [_i32, _i64, _i32, _vp, _vp, _vp, _vp]),
     "q3l_linear_fwd": (C.c_int, [_i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                  _vp]),
     "q3l_linear_dgrad": (C.c_int, [_i32, _i64, _i32, _i32, _vp, _vp, _vp,
@@ -79,8 +101,9 @@ PROTOTYPES = {
                                     _vp, _vp]),
     "q3l_attention_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "q3l_attention_bwd": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _vp,
-                                    _i64, _vp, _i64, _vp, _i64, _vp, _vp,
-                                    _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                    _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                    _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz,
+                                    _vp]),
 }
 
 _lib = None

@@ -9,7 +9,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 
 #include "../../include/q3layer.h"
@@ -105,6 +104,10 @@ q3l_status validate(const q3l_layer_cfg* c) {
   return Q3L_OK;
 }
 
+// The backward's transposed copies exist only for a bf16 layer with a
+// backward (not for the forward-only tensor-parallel share).
+bool has_transposes(const q3l_layer_cfg& c) { return c.dtype == Q3L_BF16 && !c.tp_partial; }
+
 q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
   const Dims m = dims_of(c);
   q3l_saved_layout s{};
@@ -127,14 +130,14 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
   s.f = take(m.T * (size_t)m.ffn * m.es);
   // Transposed copies for the backward (bf16): the weights, then xn^T.
   s.wt = off;
-  if (c.dtype == Q3L_BF16) {
+  if (has_transposes(c)) {
     take((size_t)m.ffn * m.d * 2);
     take((size_t)m.d * 2 * m.ffn * 2);
     take((size_t)m.qd * m.d * 2);
     take((size_t)m.d * m.nqkv * 2);
   }
   s.xnt = off;
-  if (c.dtype == Q3L_BF16) take((size_t)m.d * ((m.T + 7) / 8 * 8) * 2);
+  if (has_transposes(c)) take((size_t)m.d * ((m.T + 7) / 8 * 8) * 2);
   s.total = off;
   return s;
 }
@@ -155,7 +158,10 @@ WtLayout wt_layout(const q3l_layer_cfg& c) {
 }
 
 struct BwdWs {
-  size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart, qpart, kpart;
+  // wpart_post / wpart_in: partial-row sums of the two RMSNorm weight
+  // gradients (separate, so an input-gradient-only call leaves both for the
+  // weight-gradient call that follows it).
+  size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart_post, wpart_in, qpart, kpart;
   // bf16 only: three scratch buffers for the transposed operands of the
   // weight-gradient GEMMs ([features, Tp]).  (The transposed weights are in
   // the saved block.)
@@ -178,7 +184,8 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
   w.dqk = take(m.T * m.nqk * m.es);
   w.dqkv = take(m.T * m.nqkv * m.es);
   w.dxn = take(m.T * m.d * m.es);
-  w.wpart = take((size_t)rmsnorm_bwd_max_parts() * m.d * 4);
+  w.wpart_post = take((size_t)rmsnorm_bwd_max_parts() * m.d * 4);
+  w.wpart_in = take((size_t)rmsnorm_bwd_max_parts() * m.d * 4);
   w.qpart = take((size_t)qknorm_bwd_max_parts() * m.dh * 4);
   w.kpart = take((size_t)qknorm_bwd_max_parts() * m.dh * 4);
   if (c.dtype == Q3L_BF16) {
@@ -263,6 +270,74 @@ q3l_status check_weights(const q3l_weights* w, bool need_qk) {
   return Q3L_OK;
 }
 
+// ---- phases and their marks --------------------------------------------
+// The steps of a forward / backward call in launch order.  With marks, the
+// call records event 0 before its first kernel and event i + 1 after phase
+// i (an empty phase records its event right after the previous one).
+const char* const kFwdPhases[] = {
+    "F1 rmsnorm",
+    "F2 qkv gemm",
+    "F3-F4 qk-norm + rope",
+    "transposes for the backward",
+    "F5 attention",
+    "F6 o gemm + residual",
+    "F7 rmsnorm",
+    "F8-F9 gate/up gemm + swiglu",
+    "F10 down gemm + residual",
+};
+const char* const kBwdPhases[] = {
+    "B1 down dgrad gemm",
+    "B2 swiglu adjoint",
+    "B1 down wgrad transposes",
+    "B1 down wgrad gemm",
+    "B3 gate/up dgrad gemm",
+    "B3 gate/up wgrad transposes",
+    "B3 gate/up wgrad gemm",
+    "B4 rmsnorm bwd",
+    "B5 o dgrad gemm",
+    "B5 o wgrad transposes",
+    "B5 o wgrad gemm",
+    "B6 attention bwd",
+    "B7 qk-norm + rope bwd",
+    "B8 qkv dgrad gemm",
+    "B8 qkv wgrad transposes",
+    "B8 qkv wgrad gemm",
+    "B9 rmsnorm bwd",
+};
+constexpr int kNumFwdPhases = sizeof(kFwdPhases) / sizeof(kFwdPhases[0]);
+constexpr int kNumBwdPhases = sizeof(kBwdPhases) / sizeof(kBwdPhases[0]);
+
+struct Marks {
+  void* const* ev = nullptr;
+  int next = 0;
+  hipStream_t s = nullptr;
+  // Records the mark that ends phase `phase` (and any skipped before it).
+  hipError_t end(int phase) {
+    if (!ev) return hipSuccess;
+    while (next <= phase + 1) {
+      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev[next++]), s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+};
+
+q3l_status check_exec(const q3l_exec* ex, int nphases, bool uses_side) {
+  if (!ex) return Q3L_OK;
+  if (ex->marks) {
+    if (ex->n_marks != nphases + 1)
+      return fail(Q3L_EINVAL, "exec.n_marks is %d, this call records %d marks", ex->n_marks,
+                  nphases + 1);
+    for (int i = 0; i <= nphases; ++i)
+      if (!ex->marks[i]) return fail(Q3L_EINVAL, "exec.marks[%d] is NULL", i);
+  } else if (ex->n_marks != 0) {
+    return fail(Q3L_EINVAL, "exec.n_marks is %d but exec.marks is NULL", ex->n_marks);
+  }
+  if (uses_side && ex->side_stream && (!ex->fork_event || !ex->join_event))
+    return fail(Q3L_EINVAL, "exec.side_stream needs exec.fork_event and exec.join_event");
+  return Q3L_OK;
+}
+
 }  // namespace
 }  // namespace q3l
 
@@ -272,6 +347,12 @@ extern "C" {
 
 const char* q3l_last_error(void) { return g_err.c_str(); }
 int q3l_version(void) { return Q3L_VERSION; }
+
+int q3l_phase_count(int backward) { return backward ? kNumBwdPhases : kNumFwdPhases; }
+const char* q3l_phase_name(int backward, int i) {
+  if (i < 0 || i >= q3l_phase_count(backward)) return nullptr;
+  return backward ? kBwdPhases[i] : kFwdPhases[i];
+}
 
 q3l_status q3l_validate(const q3l_layer_cfg* cfg) {
   const q3l_status st = validate(cfg);
@@ -287,51 +368,9 @@ q3l_status q3l_saved_layout_of(const q3l_layer_cfg* cfg, q3l_saved_layout* out) 
   return Q3L_OK;
 }
 
-// ---- second stream ------------------------------------------------------
-// One per device, created on first use and kept for the process: work that
-// only depends on the call's inputs (the backward's transposed copies) runs
-// on it beside the attention step, forked from and joined back into the
-// caller's stream with events.  Default priority.  The mutex keeps one
-// call's record / wait pairs together when several host threads share a
-// device.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-hipError_t side_stream(SideStream** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream& sd = g_side[dev];
-  if (!sd.s) {
-    // All three or none: a partial failure releases what was created.
-    hipEvent_t f = nullptr, j = nullptr;
-    hipStream_t st = nullptr;
-    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) == hipSuccess &&
-        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) == hipSuccess &&
-        (e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) == hipSuccess) {
-      sd.fork = f;
-      sd.join = j;
-      sd.s = st;
-    } else {
-      if (f) (void)hipEventDestroy(f);
-      if (j) (void)hipEventDestroy(j);
-      return e;
-    }
-  }
-  *out = &sd;
-  return hipSuccess;
-}
-
 // The copies the bf16 backward reads in K-contiguous form, from inputs the
 // forward already has: the seven projection weights transposed to [in, out]
-// (one launch), and xn^T [d, Tp].
+// and xn^T [d, Tp], in one launch.
 hipError_t transposed_copies(const q3l_layer_cfg& c, const q3l_weights* w, const void* xn,
                              char* wt, char* xnt, hipStream_t s) {
   const Dims m = dims_of(c);
@@ -368,7 +407,8 @@ size_t q3l_workspace_bytes(const q3l_layer_cfg* cfg, int backward) {
 
 q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
                              const void* x, const q3l_outputs* out, void* saved,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             const q3l_exec* exec) {
   q3l_status st = validate(cfg);
   if (st != Q3L_OK) return st;
   const q3l_layer_cfg& c = *cfg;
@@ -392,9 +432,15 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
                   L.wt);
     S = workspace;
   }
+  const bool copies = saved && has_transposes(c);
+  if ((st = check_exec(exec, kNumFwdPhases, copies)) != Q3L_OK) return st;
   const Dims m = dims_of(c);
   const int dt = c.dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Marks mk;
+  mk.s = s;
+  mk.ev = exec ? exec->marks : nullptr;
+  hipStream_t side = (copies && exec) ? static_cast<hipStream_t>(exec->side_stream) : nullptr;
   float* rstd1 = reinterpret_cast<float*>(at(S, L.rstd1));
   void* xn = at(S, L.xn);
   void* qkv = at(S, L.qkv);
@@ -412,12 +458,10 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   void* f = at(S, L.f);
   const char* qkvp = static_cast<const char*>(qkv);
 
-  // The second stream (bf16 training forward) is obtained before anything
-  // is enqueued, so a failure to create it leaves no work behind.
-  SideStream* sd = nullptr;
-  if (dt == Q3L_BF16 && saved) Q3L_HIP(side_stream(&sd));
+  Q3L_HIP(mk.end(-1));
   // Step 1: input RMSNorm.
   Q3L_HIP(rmsnorm_fwd(dt, m.T, m.d, x, w->in_norm, c.eps, xn, rstd1, s));
+  Q3L_HIP(mk.end(0));
   // Step 2: q/k/v projections as one GEMM over the stacked weights.
   {
     GemmArgs g{};
@@ -429,10 +473,16 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     g.epi = epi_store(qkv, m.nqkv, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
+  Q3L_HIP(mk.end(1));
   // Steps 3-4: per-head q/k RMSNorm, then RoPE.
   Q3L_HIP(rope_table(m.L, m.dh, c.rope_theta, cs, sn, s));
   Q3L_HIP(qknorm_rope_fwd(dt, m.B, m.L, m.hq, m.hkv, m.dh, c.qk_norm, c.eps, qkv,
                           m.nqkv, w->q_norm, w->k_norm, cs, sn, qkr, m.nqk, rq, rk, s));
+  Q3L_HIP(mk.end(2));
+  // The backward's transposed copies: on the caller's stream here, or on the
+  // caller's second stream beside the attention step.
+  if (copies && !side) Q3L_HIP(transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), s));
+  Q3L_HIP(mk.end(3));
   // Step 5: causal GQA attention.
   {
     AttnArgs a{};
@@ -441,19 +491,17 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.k = static_cast<const char*>(qkr) + (size_t)m.qd * m.es; a.ldk = m.nqk;
     a.v = qkvp + (size_t)(m.qd + m.kvd) * m.es; a.ldv = m.nqkv;
     a.o = ao; a.ldo = m.qd; a.lse = lse;
-    if (sd) {
-      // The backward's transposed copies on the second stream, beside the
-      // attention kernel.  The lock keeps this call's record / wait pairs on
-      // the shared events together.
-      std::lock_guard<std::mutex> lk(g_side_mu);
-      Q3L_HIP(hipEventRecord(sd->fork, s));
-      Q3L_HIP(hipStreamWaitEvent(sd->s, sd->fork, 0));
-      const hipError_t e1 = transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), sd->s);
-      const hipError_t e2 = hipEventRecord(sd->join, sd->s);
+    if (side) {
+      hipEvent_t fork = static_cast<hipEvent_t>(exec->fork_event);
+      hipEvent_t join = static_cast<hipEvent_t>(exec->join_event);
+      Q3L_HIP(hipEventRecord(fork, s));
+      Q3L_HIP(hipStreamWaitEvent(side, fork, 0));
+      const hipError_t e1 = transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), side);
+      const hipError_t e2 = hipEventRecord(join, side);
       const hipError_t e3 = attn_fwd(dt, a, s);
       // Joined whatever happened above, so nothing of this call is left
       // running unordered with the caller's stream.
-      const hipError_t e4 = hipStreamWaitEvent(s, sd->join, 0);
+      const hipError_t e4 = hipStreamWaitEvent(s, join, 0);
       Q3L_HIP(e1);
       Q3L_HIP(e2);
       Q3L_HIP(e3);
@@ -462,6 +510,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
       Q3L_HIP(attn_fwd(dt, a, s));
     }
   }
+  Q3L_HIP(mk.end(4));
   // Steps 6-7: o_proj with the residual in the epilogue.
   {
     GemmArgs g{};
@@ -477,11 +526,14 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     }
     Q3L_HIP(gemm(dt, g, s));
   }
+  Q3L_HIP(mk.end(5));
   // Step 8: post-attention RMSNorm.
   Q3L_HIP(rmsnorm_fwd(dt, m.T, m.d, h, w->post_norm, c.eps, hn, rstd2, s));
+  Q3L_HIP(mk.end(6));
   // Step 9: gate/up as one GEMM over interleaved rows, silu(g) * u fused.
   Q3L_HIP(gemm(dt, swiglu_args(hn, m.d, (int)m.T, w->gate, w->up, m.ffn, f,
                                saved ? gu : nullptr), s));
+  Q3L_HIP(mk.end(7));
   // Steps 9-10: down projection with the residual in the epilogue.
   {
     GemmArgs g{};
@@ -496,6 +548,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     }
     Q3L_HIP(gemm(dt, g, s));
   }
+  Q3L_HIP(mk.end(8));
   g_err.clear();
   return Q3L_OK;
 }
@@ -503,16 +556,24 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
 q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
                               const void* x, const void* dy, const void* saved,
                               void* dx, const q3l_grads* grads, int flags,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const q3l_exec* exec) {
   q3l_status st = validate(cfg);
   if (st != Q3L_OK) return st;
   const q3l_layer_cfg& c = *cfg;
   if (c.tp_partial)
     return fail(Q3L_EUNSUPPORTED, "backward of a tp_partial layer is not provided");
   if ((st = check_weights(w, c.qk_norm != 0)) != Q3L_OK) return st;
-  if (flags & ~(Q3L_BWD_INPUT | Q3L_BWD_WEIGHT | Q3L_BWD_ACCUMULATE))
+  if (flags & ~(Q3L_BWD_INPUT | Q3L_BWD_WEIGHT | Q3L_BWD_ACCUMULATE | Q3L_BWD_DEFERRED_WEIGHT))
     return fail(Q3L_EINVAL, "unknown flag bits 0x%x", flags);
   const bool want_dx = flags & Q3L_BWD_INPUT, want_w = flags & Q3L_BWD_WEIGHT;
+  const bool deferred = flags & Q3L_BWD_DEFERRED_WEIGHT;
+  if (deferred && (!want_w || want_dx))
+    return fail(Q3L_EINVAL, "Q3L_BWD_DEFERRED_WEIGHT goes with Q3L_BWD_WEIGHT and "
+                "without Q3L_BWD_INPUT");
+  // The input-gradient chain runs unless a previous INPUT-only call on this
+  // workspace already ran it.
+  const bool chain = !deferred;
   const int acc = (flags & Q3L_BWD_ACCUMULATE) ? 1 : 0;
   Q3L_CHECK_PTR(x, "x");
   Q3L_CHECK_PTR(dy, "dy");
@@ -539,12 +600,21 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (workspace_bytes < W.total)
     return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes,
                 W.total);
-  if (!want_dx && !want_w) { g_err.clear(); return Q3L_OK; }
+  if ((st = check_exec(exec, kNumBwdPhases, false)) != Q3L_OK) return st;
 
   const q3l_saved_layout L = saved_layout(c);
   const Dims m = dims_of(c);
   const int dt = c.dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Marks mk;
+  mk.s = s;
+  mk.ev = exec ? exec->marks : nullptr;
+  Q3L_HIP(mk.end(-1));
+  if (!want_dx && !want_w) {
+    Q3L_HIP(mk.end(kNumBwdPhases - 1));
+    g_err.clear();
+    return Q3L_OK;
+  }
   const float* rstd1 = reinterpret_cast<const float*>(at(saved, L.rstd1));
   const void* xn = at(saved, L.xn);
   const char* qkv = at(saved, L.qkv);
@@ -568,10 +638,15 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   char* dqk = at(workspace, W.dqk);
   char* dqkv = at(workspace, W.dqkv);
   void* dxn = at(workspace, W.dxn);
-  float* wpart = reinterpret_cast<float*>(at(workspace, W.wpart));
+  float* wpart_post = reinterpret_cast<float*>(at(workspace, W.wpart_post));
+  float* wpart_in = reinterpret_cast<float*>(at(workspace, W.wpart_in));
   float* qpart = reinterpret_cast<float*>(at(workspace, W.qpart));
   float* kpart = reinterpret_cast<float*>(at(workspace, W.kpart));
   const int T = (int)m.T;
+  // Partial-row counts of the norm-weight reductions: fixed by the shapes,
+  // so a deferred weight-gradient call knows them without the chain.
+  const int np_norm = rmsnorm_bwd_parts(dt, m.T, m.d);
+  const int np_qk = qknorm_bwd_parts(m.T, m.hq + m.hkv, m.dh);
 
   // bf16: every backward GEMM runs in the matrix-core kernel's K-contiguous
   // form.  The weights transposed to [in, out], and xn^T, come from the
@@ -591,33 +666,36 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   char* tB = bt ? at(workspace, W.tB) : nullptr;
   char* tC = bt ? at(workspace, W.tC) : nullptr;
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
-  // feature counts; A/B activations with row strides lda/ldb).  bf16: A and
-  // B are transposed into tA and tB (tA_, tB_ when given); a_done / b_done
-  // say that transpose is already there.
-  auto wgrad = [&](const void* A, int lda, int ma, const void* B, int ldb, int nb,
-                   Epilogue e, bool a_done = false, bool b_done = false,
-                   char* tA_ = nullptr, char* tB_ = nullptr) -> hipError_t {
+  // feature counts; A/B activations with row strides lda/ldb), as two
+  // phases: the operand transposes (bf16: A into ta, B into tb, skipping
+  // those marked done; one launch) and the GEMM.
+  auto wgrad = [&](int phase_t, const void* A, int lda, int ma, const void* B, int ldb,
+                   int nb, Epilogue e, char* ta, char* tb, bool a_done,
+                   bool b_done) -> hipError_t {
     GemmArgs g{};
     if (bt) {
-      char* ta = tA_ ? tA_ : tA;
-      char* tb = tB_ ? tB_ : tB;
       TransposeJob jobs[2];
       int nj = 0;
       if (!a_done) jobs[nj++] = TransposeJob{A, lda, ta, Tp, T, Tp, ma};
       if (!b_done) jobs[nj++] = TransposeJob{B, ldb, tb, Tp, T, Tp, nb};
-      const hipError_t err = transpose_bf16_batch(jobs, nj, s);   // one launch
+      hipError_t err = transpose_bf16_batch(jobs, nj, s);
       if (err != hipSuccess) return err;
+      if ((err = mk.end(phase_t)) != hipSuccess) return err;
       g.a = kop(ta, Tp, ma);
       g.b = kop(tb, Tp, nb);
       g.K = Tp;
     } else {
+      const hipError_t err = mk.end(phase_t);
+      if (err != hipSuccess) return err;
       g.a = rop(A, lda, ma);
       g.b = rop(B, ldb, nb);
       g.K = T;
     }
     g.M = ma; g.N = nb;
     g.epi = e;
-    return gemm(dt, g, s);
+    const hipError_t err = gemm(dt, g, s);
+    if (err != hipSuccess) return err;
+    return mk.end(phase_t + 1);
   };
 
   // Step 9 (down_proj): df = dy W_down.  fp32: fused with the SwiGLU adjoint
@@ -625,7 +703,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   // separate pass turns it into dg | du, writing the transposes the two
   // weight gradients read as well: [dg du]^T and f^T (an epilogue that reads
   // g, u would hold the matrix cores idle while it waits on memory).
-  {
+  if (chain) {
     GemmArgs g{};
     g.a = kop(dy, m.d, T);
     g.b = bt ? kop(wt_down, m.d, m.ffn) : rop(w->down, m.ffn, m.ffn);
@@ -639,15 +717,21 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     }
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (bt)
+  Q3L_HIP(mk.end(0));
+  if (bt && chain)
     Q3L_HIP(swiglu_bwd_bf16(T, Tp, m.ffn, dgu, 2 * (int64_t)m.ffn, gu, 2 * (int64_t)m.ffn,
                             dgu, 2 * (int64_t)m.ffn, want_w ? tA : nullptr, Tp,
                             want_w ? tB : nullptr, s));
+  if (bt && deferred)   // [dg du]^T and f^T from the dg | du the INPUT call left
+    Q3L_HIP(swiglu_transposes_bf16(T, Tp, m.ffn, gu, 2 * (int64_t)m.ffn, dgu,
+                                   2 * (int64_t)m.ffn, tA, Tp, tB, s));
+  Q3L_HIP(mk.end(1));
   if (want_w)  // dW_down = dy^T f  (bf16: f^T already in tB)
-    Q3L_HIP(wgrad(dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc),
-                  /*a_done=*/false, /*b_done=*/bt, tC, nullptr));
+    Q3L_HIP(wgrad(2, dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc), tC,
+                  tB, false, bt));
+  Q3L_HIP(mk.end(3));
   // Step 9 (gate/up): dhn = dg W_gate + du W_up (one GEMM over stacked K).
-  {
+  if (chain) {
     GemmArgs g{};
     g.a = kop(dgu, 2 * (int64_t)m.ffn, T);
     if (bt) {
@@ -660,19 +744,22 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     g.epi = epi_store(dhn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (want_w) {  // dW_gate | dW_up = [dg du]^T hn
+  Q3L_HIP(mk.end(4));
+  if (want_w) {  // dW_gate | dW_up = [dg du]^T hn  ([dg du]^T already in tA)
     Epilogue e = epi_wgrad(grads->gate, m.d, acc);
     e.cs[1] = grads->up; e.cstart[1] = m.ffn; e.cnseg = 2;
-    Q3L_HIP(wgrad(dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e, /*a_done=*/bt));
+    Q3L_HIP(wgrad(5, dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e, tA, tB, bt, false));
   }
+  Q3L_HIP(mk.end(6));
   // Steps 8 and 10: post-attention RMSNorm adjoint plus the residual dy.
-  {
+  if (chain) {
     int np = 0;
-    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dhn, h, rstd2, w->post_norm, dy, dh, wpart, &np, s));
-    if (want_w) Q3L_HIP(reduce_rows(wpart, np, m.d, grads->post_norm, acc, s));
+    Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dhn, h, rstd2, w->post_norm, dy, dh, wpart_post, &np, s));
   }
+  if (want_w) Q3L_HIP(reduce_rows(wpart_post, np_norm, m.d, grads->post_norm, acc, s));
+  Q3L_HIP(mk.end(7));
   // Step 6: dO = dh W_o.
-  {
+  if (chain) {
     GemmArgs g{};
     g.a = kop(dh, m.d, T);
     g.b = bt ? kop(wt_o, m.d, m.qd) : rop(w->o, m.qd, m.qd);
@@ -680,10 +767,13 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     g.epi = epi_store(dO, m.qd, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
+  Q3L_HIP(mk.end(8));
   if (want_w)  // dW_o = dh^T O
-    Q3L_HIP(wgrad(dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc)));
+    Q3L_HIP(wgrad(9, dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc), tA, tB,
+                  false, false));
+  Q3L_HIP(mk.end(10));
   // Step 5: attention backward (P recomputed from the log-sum-exp).
-  {
+  if (chain) {
     AttnArgs a{};
     a.B = m.B; a.L = m.L; a.h_q = m.hq; a.h_kv = m.hkv; a.d_h = m.dh;
     a.q = qkr; a.ldq = m.nqk;
@@ -696,18 +786,19 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.delta = delta;
     Q3L_HIP(attn_bwd(dt, a, s));
   }
+  Q3L_HIP(mk.end(11));
   // Steps 4-3: RoPE adjoint and q/k RMSNorm adjoint.
-  {
+  if (chain) {
     int np = 0;
     Q3L_HIP(qknorm_rope_bwd(dt, m.B, m.L, m.hq, m.hkv, m.dh, c.qk_norm, dqk, m.nqk,
                             qkv, m.nqkv, w->q_norm, w->k_norm, rq, rk, cs, sn, dqkv,
                             m.nqkv, qpart, kpart, &np, s));
-    if (want_w && c.qk_norm) {
-      Q3L_HIP(reduce_rows2(qpart, kpart, np, m.dh, grads->q_norm, grads->k_norm, acc, s));
-    }
   }
+  if (want_w && c.qk_norm)
+    Q3L_HIP(reduce_rows2(qpart, kpart, np_qk, m.dh, grads->q_norm, grads->k_norm, acc, s));
+  Q3L_HIP(mk.end(12));
   // Step 2: dxn = [dq dk dv] [W_q; W_k; W_v].
-  {
+  if (chain) {
     GemmArgs g{};
     g.a = kop(dqkv, m.nqkv, T);
     if (bt) {
@@ -721,22 +812,24 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     g.epi = epi_store(dxn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
   }
-  if (want_w) {  // dW_q | dW_k | dW_v = [dq dk dv]^T xn
+  Q3L_HIP(mk.end(13));
+  if (want_w) {  // dW_q | dW_k | dW_v = [dq dk dv]^T xn  (bf16: xn^T saved)
     Epilogue e = epi_wgrad(grads->q, m.d, acc);
     e.cs[1] = grads->k; e.cstart[1] = m.qd;
     e.cs[2] = grads->v; e.cstart[2] = m.qd + m.kvd;
     e.cnseg = 3;
-    // bf16: xn^T is in the saved block (written by the forward).
-    Q3L_HIP(wgrad(dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e, false, bt, nullptr,
-                  const_cast<char*>(xnt)));
+    Q3L_HIP(wgrad(14, dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e, tA, const_cast<char*>(xnt),
+                  false, bt));
   }
+  Q3L_HIP(mk.end(15));
   // Step 1: input RMSNorm adjoint plus the attention residual dh.
-  {
+  if (chain) {
     int np = 0;
     Q3L_HIP(rmsnorm_bwd(dt, m.T, m.d, dxn, x, rstd1, w->in_norm, dh,
-                        want_dx ? dx : nullptr, wpart, &np, s));
-    if (want_w) Q3L_HIP(reduce_rows(wpart, np, m.d, grads->in_norm, acc, s));
+                        want_dx ? dx : nullptr, wpart_in, &np, s));
   }
+  if (want_w) Q3L_HIP(reduce_rows(wpart_in, np_norm, m.d, grads->in_norm, acc, s));
+  Q3L_HIP(mk.end(16));
   g_err.clear();
   return Q3L_OK;
 }
@@ -755,10 +848,138 @@ q3l_status q3l_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t n, const void* x
   return Q3L_OK;
 }
 
+size_t q3l_rmsnorm_bwd_workspace_bytes(int32_t n) {
+  if (n <= 0) return 0;
+  return up((size_t)rmsnorm_bwd_max_parts() * n * 4);
+}
+
+q3l_status q3l_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t n, const void* dy,
+                           const void* x, const float* rstd, const void* w, const void* resid,
+                           void* dx, float* dw, int accumulate, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
+  if (rows <= 0 || n <= 0 || n % 8 != 0)
+    return fail(Q3L_EINVAL, "need rows > 0 and n a positive multiple of 8");
+  if (n > 8192) return fail(Q3L_EUNSUPPORTED, "n=%d exceeds 8192", n);
+  if (rows > (1LL << 30)) return fail(Q3L_EUNSUPPORTED, "rows exceed 2^30");
+  Q3L_CHECK_PTR(dy, "dy"); Q3L_CHECK_PTR(x, "x"); Q3L_CHECK_PTR(rstd, "rstd");
+  Q3L_CHECK_PTR(w, "w"); Q3L_CHECK_PTR(dx, "dx"); Q3L_CHECK_PTR(workspace, "workspace");
+  if (resid && !aligned16(resid)) return fail(Q3L_EALIGN, "resid is not 16-byte aligned");
+  if (dw && !aligned16(dw)) return fail(Q3L_EALIGN, "dw is not 16-byte aligned");
+  if (workspace_bytes < q3l_rmsnorm_bwd_workspace_bytes(n))
+    return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes,
+                q3l_rmsnorm_bwd_workspace_bytes(n));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int np = 0;
+  float* part = static_cast<float*>(workspace);
+  Q3L_HIP(rmsnorm_bwd(dtype, rows, n, dy, x, rstd, w, resid, dx, part, &np, s));
+  if (dw) Q3L_HIP(reduce_rows(part, np, n, dw, accumulate ? 1 : 0, s));
+  return Q3L_OK;
+}
+
+q3l_status q3l_rope_table(int32_t L, int32_t d_h, float theta, float* cos_t, float* sin_t,
+                          void* stream) {
+  if (L <= 0 || (d_h != 64 && d_h != 128)) return fail(Q3L_EINVAL, "need L > 0, d_h 64 or 128");
+  if (!(theta > 0.0f) || !std::isfinite(theta)) return fail(Q3L_EINVAL, "bad theta");
+  if ((int64_t)L * d_h > (1LL << 30)) return fail(Q3L_EUNSUPPORTED, "L too long");
+  Q3L_CHECK_PTR(cos_t, "cos_t"); Q3L_CHECK_PTR(sin_t, "sin_t");
+  Q3L_HIP(rope_table(L, d_h, theta, cos_t, sin_t, static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
+static q3l_status check_heads(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
+                              int32_t d_h) {
+  if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
+  if (B <= 0 || L <= 0 || h_q <= 0 || h_kv <= 0)
+    return fail(Q3L_EINVAL, "need positive B, L and heads");
+  if (d_h != 64 && d_h != 128) return fail(Q3L_EUNSUPPORTED, "d_h must be 64 or 128");
+  if ((int64_t)B * L * (h_q + h_kv) * d_h > (1LL << 40))
+    return fail(Q3L_EUNSUPPORTED, "sizes exceed the index range");
+  return Q3L_OK;
+}
+
+q3l_status q3l_qknorm_rope_fwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
+                               int32_t d_h, int32_t qk_norm, float eps, const void* in,
+                               int64_t ld_in, const void* wq, const void* wk,
+                               const float* cos_t, const float* sin_t, void* out,
+                               int64_t ld_out, float* rstd_q, float* rstd_k, void* stream) {
+  q3l_status st = check_heads(dtype, B, L, h_q, h_kv, d_h);
+  if (st != Q3L_OK) return st;
+  if (qk_norm != 0 && qk_norm != 1) return fail(Q3L_EINVAL, "qk_norm must be 0 or 1");
+  const int64_t w = (int64_t)(h_q + h_kv) * d_h;
+  if (ld_in < w || ld_out < w || ld_in % 8 || ld_out % 8)
+    return fail(Q3L_EINVAL, "row strides below (h_q + h_kv) * d_h or not multiples of 8");
+  Q3L_CHECK_PTR(in, "in"); Q3L_CHECK_PTR(out, "out");
+  Q3L_CHECK_PTR(cos_t, "cos_t"); Q3L_CHECK_PTR(sin_t, "sin_t");
+  if (qk_norm) {
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(Q3L_EINVAL, "bad eps");
+    Q3L_CHECK_PTR(wq, "wq"); Q3L_CHECK_PTR(wk, "wk");
+    Q3L_CHECK_PTR(rstd_q, "rstd_q"); Q3L_CHECK_PTR(rstd_k, "rstd_k");
+  }
+  Q3L_HIP(qknorm_rope_fwd(dtype, B, L, h_q, h_kv, d_h, qk_norm, eps, in, ld_in, wq, wk, cos_t,
+                          sin_t, out, ld_out, rstd_q, rstd_k, static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
+size_t q3l_qknorm_rope_bwd_workspace_bytes(int32_t d_h) {
+  if (d_h != 64 && d_h != 128) return 0;
+  return 2 * up((size_t)qknorm_bwd_max_parts() * d_h * 4);
+}
+
+q3l_status q3l_qknorm_rope_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
+                               int32_t d_h, int32_t qk_norm, const void* g, int64_t ld_g,
+                               const void* pre, int64_t ld_pre, const void* wq,
+                               const void* wk, const float* rstd_q, const float* rstd_k,
+                               const float* cos_t, const float* sin_t, void* out,
+                               int64_t ld_out, float* dwq, float* dwk, int accumulate,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  q3l_status st = check_heads(dtype, B, L, h_q, h_kv, d_h);
+  if (st != Q3L_OK) return st;
+  if (qk_norm != 0 && qk_norm != 1) return fail(Q3L_EINVAL, "qk_norm must be 0 or 1");
+  const int64_t w = (int64_t)(h_q + h_kv) * d_h;
+  if (ld_g < w || ld_out < w || ld_g % 8 || ld_out % 8 ||
+      (qk_norm && (ld_pre < w || ld_pre % 8)))
+    return fail(Q3L_EINVAL, "row strides below (h_q + h_kv) * d_h or not multiples of 8");
+  Q3L_CHECK_PTR(g, "g"); Q3L_CHECK_PTR(out, "out");
+  Q3L_CHECK_PTR(cos_t, "cos_t"); Q3L_CHECK_PTR(sin_t, "sin_t");
+  Q3L_CHECK_PTR(workspace, "workspace");
+  if (qk_norm) {
+    Q3L_CHECK_PTR(pre, "pre");
+    Q3L_CHECK_PTR(wq, "wq"); Q3L_CHECK_PTR(wk, "wk");
+    Q3L_CHECK_PTR(rstd_q, "rstd_q"); Q3L_CHECK_PTR(rstd_k, "rstd_k");
+  }
+  if ((dwq == nullptr) != (dwk == nullptr))
+    return fail(Q3L_EINVAL, "dwq and dwk are both given or both NULL");
+  if ((dwq && !aligned16(dwq)) || (dwk && !aligned16(dwk)))
+    return fail(Q3L_EALIGN, "dwq / dwk not 16-byte aligned");
+  if (workspace_bytes < q3l_qknorm_rope_bwd_workspace_bytes(d_h))
+    return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes,
+                q3l_qknorm_rope_bwd_workspace_bytes(d_h));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* qpart = static_cast<float*>(workspace);
+  float* kpart = reinterpret_cast<float*>(
+      static_cast<char*>(workspace) + up((size_t)qknorm_bwd_max_parts() * d_h * 4));
+  int np = 0;
+  Q3L_HIP(qknorm_rope_bwd(dtype, B, L, h_q, h_kv, d_h, qk_norm, g, ld_g, pre, ld_pre, wq, wk,
+                          rstd_q, rstd_k, cos_t, sin_t, out, ld_out, qpart, kpart, &np, s));
+  if (dwq && qk_norm) Q3L_HIP(reduce_rows2(qpart, kpart, np, d_h, dwq, dwk, accumulate ? 1 : 0, s));
+  return Q3L_OK;
+}
+
+// The bf16 GEMM addresses each operand with 32-bit byte offsets: an [M, N]
+// or [M, K] activation and an [N, K] weight must each stay below 2 GiB (with
+// the 8 rows of padding the loads may touch).
 static q3l_status check_mnk(int32_t dtype, int64_t M, int32_t N, int32_t K) {
   if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
   if (M < 0 || M > (1LL << 30) || N <= 0 || K <= 0 || N % 8 != 0 || K % 8 != 0)
     return fail(Q3L_EINVAL, "need 0 <= M <= 2^30 and N, K positive multiples of 8");
+  if (dtype == Q3L_BF16) {
+    const int64_t wide = std::max<int64_t>(N, K);
+    if ((M + 8) * wide * 2 >= (1LL << 31) || ((int64_t)N + 8) * K * 2 >= (1LL << 31) ||
+        ((int64_t)K + 8) * N * 2 >= (1LL << 31))
+      return fail(Q3L_EUNSUPPORTED, "M=%lld N=%d K=%d: an operand exceeds the 2 GiB offset "
+                  "range of the bf16 GEMM", (long long)M, N, K);
+  }
   return Q3L_OK;
 }
 
@@ -797,12 +1018,12 @@ q3l_status q3l_linear_wgrad(int32_t dtype, int64_t M, int32_t N, int32_t K,
   q3l_status st = check_mnk(dtype, M, N, K);
   if (st != Q3L_OK) return st;
   Q3L_CHECK_PTR(dy, "dy"); Q3L_CHECK_PTR(a, "a"); Q3L_CHECK_PTR(dw, "dw");
+  if (M == 0) return fail(Q3L_EINVAL, "M must be positive for a weight gradient");
   GemmArgs g{};
   g.a = rop(dy, N, N);
   g.b = rop(a, K, K);
   g.M = N; g.N = K; g.K = (int)M;
   g.epi = epi_wgrad(dw, K, accumulate ? 1 : 0);
-  if (M == 0) return fail(Q3L_EINVAL, "M must be positive for a weight gradient");
   Q3L_HIP(gemm(dtype, g, static_cast<hipStream_t>(stream)));
   return Q3L_OK;
 }
@@ -810,13 +1031,36 @@ q3l_status q3l_linear_wgrad(int32_t dtype, int64_t M, int32_t N, int32_t K,
 q3l_status q3l_swiglu_fwd(int32_t dtype, int64_t M, int32_t N, int32_t K, const void* hn,
                           const void* gate, const void* up, void* f, void* gu,
                           void* stream) {
+  // The fused GEMM's logical width is the interleaved gate/up pair, 2 N
+  // rounded up to 64 columns; g | u is an [M, 2N] output.
   q3l_status st = check_mnk(dtype, M, N, K);
+  if (st == Q3L_OK && N > (1 << 28)) st = fail(Q3L_EUNSUPPORTED, "N=%d too large", N);
+  if (st == Q3L_OK) st = check_mnk(dtype, M, 2 * ((N + 31) / 32 * 32), K);
   if (st != Q3L_OK) return st;
   Q3L_CHECK_PTR(hn, "hn"); Q3L_CHECK_PTR(gate, "gate"); Q3L_CHECK_PTR(up, "up");
   Q3L_CHECK_PTR(f, "f");
   if (gu && !aligned16(gu)) return fail(Q3L_EALIGN, "gu is not 16-byte aligned");
   Q3L_HIP(gemm(dtype, swiglu_args(hn, K, (int)M, gate, up, N, f, gu),
                static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
+q3l_status q3l_swiglu_bwd(int32_t dtype, int64_t M, int32_t N, const void* df, const void* gu,
+                          void* dgu, void* stream) {
+  if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
+  if (M < 0 || M > (1LL << 30) - 8 || N <= 0 || N % 8 != 0 || N > (1 << 29))
+    return fail(Q3L_EINVAL, "need 0 <= M < 2^30 and N a positive multiple of 8");
+  Q3L_CHECK_PTR(df, "df"); Q3L_CHECK_PTR(gu, "gu"); Q3L_CHECK_PTR(dgu, "dgu");
+  if (dgu == gu) return fail(Q3L_EINVAL, "dgu may not alias gu");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == Q3L_BF16) {
+    Q3L_HIP(swiglu_bwd_bf16((int)M, (int)pad8(M), N, df, N, gu, 2 * (int64_t)N, dgu,
+                            2 * (int64_t)N, nullptr, 0, nullptr, s));
+  } else {
+    Q3L_HIP(swiglu_bwd_f32(M, N, static_cast<const float*>(df), N,
+                           static_cast<const float*>(gu), 2 * (int64_t)N,
+                           static_cast<float*>(dgu), 2 * (int64_t)N, s));
+  }
   return Q3L_OK;
 }
 
@@ -873,9 +1117,9 @@ size_t q3l_attention_bwd_workspace_bytes(int32_t B, int32_t L, int32_t h_q) {
 q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
                              int32_t d_h, const void* q, int64_t ldq, const void* k,
                              int64_t ldk, const void* v, int64_t ldv, const void* o,
-                             const void* dout, int64_t ldo, const float* lse, void* dq,
-                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int64_t ldo, const void* dout, int64_t lddo, const float* lse,
+                             void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   q3l_status st = check_attn(dtype, B, L, h_q, h_kv, d_h);
   if (st != Q3L_OK) return st;
   Q3L_CHECK_PTR(q, "q"); Q3L_CHECK_PTR(k, "k"); Q3L_CHECK_PTR(v, "v");
@@ -885,16 +1129,18 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   if (workspace_bytes < q3l_attention_bwd_workspace_bytes(B, L, h_q))
     return fail(Q3L_EINVAL, "workspace too small");
   if (ldq < (int64_t)h_q * d_h || ldk < (int64_t)h_kv * d_h || ldv < (int64_t)h_kv * d_h ||
-      ldo < (int64_t)h_q * d_h || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
+      ldo < (int64_t)h_q * d_h || lddo < (int64_t)h_q * d_h || ldq % 8 || ldk % 8 ||
+      ldv % 8 || ldo % 8 || lddo % 8)
     return fail(Q3L_EINVAL, "row strides too small or not multiples of 8");
   if ((st = check_attn_range(dtype, B, L, h_q,
-                             std::max(std::max(ldq, ldk), std::max(ldv, ldo)))) != Q3L_OK)
+                             std::max(std::max(std::max(ldq, ldk), std::max(ldv, ldo)),
+                                      lddo))) != Q3L_OK)
     return st;
   AttnArgs a{};
   a.B = B; a.L = L; a.h_q = h_q; a.h_kv = h_kv; a.d_h = d_h;
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv;
   a.o = const_cast<void*>(o); a.ldo = ldo; a.lse = const_cast<float*>(lse);
-  a.dout = dout; a.lddo = ldo; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dout = dout; a.lddo = lddo; a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(workspace);
   Q3L_HIP(attn_bwd(dtype, a, static_cast<hipStream_t>(stream)));
   return Q3L_OK;

@@ -538,15 +538,22 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
 
 constexpr int kQkBwdParts = 1024;
 
+// Workgroups (= partial rows of the weight gradient) of the RMSNorm
+// backward: bf16 at least 8 rows per workgroup, so the loads of the next rows
+// overlap; fp32 at least 4 rows per wave.
+int64_t rmsnorm_bwd_grid(int dtype, int64_t rows) {
+  int64_t grid = dtype == 1 ? cdiv(rows, 8) : cdiv(rows, 4 * 4);
+  if (grid > kNormBwdParts) grid = kNormBwdParts;
+  if (grid < 1) grid = 1;
+  return grid;
+}
+
 template <class T>
 hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
                          const float* rstd, const void* w, const void* resid, void* dx,
                          float* wpart, int* nparts, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    // At least 8 rows per workgroup, so the loads of the next rows overlap.
-    int64_t grid = cdiv(rows, 8);
-    if (grid > kNormBwdParts) grid = kNormBwdParts;
-    if (grid < 1) grid = 1;
+    const int64_t grid = rmsnorm_bwd_grid(1, rows);
     *nparts = (int)grid;
     const int cpt = (int)cdiv(n, 8 * 256);
 #define Q3L_RB16K(C, R)                                                              \
@@ -565,9 +572,7 @@ hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
     return hipGetLastError();
   }
   const int cpl = (int)cdiv(n, 512);
-  int64_t grid = cdiv(rows, 4 * 4);  // at least 4 rows per wave
-  if (grid > kNormBwdParts) grid = kNormBwdParts;
-  if (grid < 1) grid = 1;
+  const int64_t grid = rmsnorm_bwd_grid(0, rows);
   *nparts = (int)grid;
   const size_t shm = (size_t)n * sizeof(float);
 #define Q3L_RB(C)                                                              \
@@ -584,10 +589,27 @@ hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
   return hipGetLastError();
 }
 
+// Workgroups (= partial rows) of the q/k norm backward: many small ones, so
+// enough waves keep loads in flight.
+int64_t qknorm_bwd_grid(int64_t tokens, int heads, int d_h) {
+  const int per_block = 256 / (d_h / 8);
+  int64_t grid = cdiv(tokens * heads, (int64_t)per_block * 8);
+  if (grid > kQkBwdParts) grid = kQkBwdParts;
+  if (grid < 1) grid = 1;
+  return grid;
+}
+
 }  // namespace
 
 int rmsnorm_bwd_max_parts() { return kNormBwdParts; }
 int qknorm_bwd_max_parts() { return kQkBwdParts; }
+int rmsnorm_bwd_parts(int dtype, int64_t rows, int n) {
+  (void)n;
+  return (int)rmsnorm_bwd_grid(dtype, rows);
+}
+int qknorm_bwd_parts(int64_t tokens, int heads, int d_h) {
+  return (int)qknorm_bwd_grid(tokens, heads, d_h);
+}
 
 hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
                        const void* w, float eps, void* y, float* rstd,
@@ -678,13 +700,8 @@ hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
                            float* wq_part, float* wk_part, int* nparts,
                            hipStream_t s) {
   const int64_t tokens = (int64_t)B * L;
-  const int64_t items = tokens * (h_q + h_kv);
-  const int per_block = 256 / (d_h / 8);
-  // Many small workgroups (enough waves to keep the loads in flight); each
-  // writes one partial row of the q/k norm weight gradients.
-  int64_t grid = cdiv(items, (int64_t)per_block * 8);
-  if (grid > kQkBwdParts) grid = kQkBwdParts;
-  if (grid < 1) grid = 1;
+  // Each workgroup writes one partial row of the q/k norm weight gradients.
+  const int64_t grid = qknorm_bwd_grid(tokens, h_q + h_kv, d_h);
   *nparts = (int)grid;
 #define Q3L_QB(T, D)                                                            \
   hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T, D>), dim3(grid), dim3(256), 0, s, \

@@ -88,6 +88,14 @@ hipError_t transpose_bf16_batch(const TransposeJob* jobs, int n, hipStream_t s);
 hipError_t swiglu_bwd_bf16(int T, int Tp, int ffn, const void* df, int64_t ld_df,
                            const void* gu, int64_t ld_gu, void* dgu, int64_t ld_dgu,
                            void* dguT, int64_t ld_t, void* fT, hipStream_t s);
+// Only the transposed copies of the above, from a dgu an earlier
+// swiglu_bwd_bf16 wrote: bitwise the dguT and fT the fused form writes.
+hipError_t swiglu_transposes_bf16(int T, int Tp, int ffn, const void* gu, int64_t ld_gu,
+                                  const void* dgu, int64_t ld_dgu, void* dguT, int64_t ld_t,
+                                  void* fT, hipStream_t s);
+// fp32 SwiGLU adjoint, dgu = [dg | du] from df and g | u.
+hipError_t swiglu_bwd_f32(int64_t M, int ffn, const float* df, int64_t ld_df, const float* gu,
+                          int64_t ld_gu, float* dgu, int64_t ld_dgu, hipStream_t s);
 
 // ---- norms / RoPE / elementwise (dtype: 0 fp32, 1 bf16) -------------------
 hipError_t rmsnorm_fwd(int dtype, int64_t rows, int n, const void* x,
@@ -101,6 +109,8 @@ hipError_t rmsnorm_bwd(int dtype, int64_t rows, int n, const void* dy,
                        const void* resid, void* dx, float* wpart, int* nparts,
                        hipStream_t s);
 int rmsnorm_bwd_max_parts();
+// The partial-row count rmsnorm_bwd reports for these sizes.
+int rmsnorm_bwd_parts(int dtype, int64_t rows, int n);
 // out[n] (+)= sum_p part[p][n]
 hipError_t reduce_rows(const float* part, int nparts, int n, float* out,
                        int accumulate, hipStream_t s);
@@ -126,6 +136,8 @@ hipError_t qknorm_rope_bwd(int dtype, int B, int L, int h_q, int h_kv,
                            float* wq_part, float* wk_part, int* nparts,
                            hipStream_t s);
 int qknorm_bwd_max_parts();
+// The partial-row count qknorm_rope_bwd reports (heads = h_q + h_kv).
+int qknorm_bwd_parts(int64_t tokens, int heads, int d_h);
 
 // ---- attention ------------------------------------------------------------
 struct AttnArgs {

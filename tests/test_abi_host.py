@@ -145,19 +145,19 @@ def test_forward_rejects_null_and_misaligned_pointers_before_launch(abi, lib):
     out = abi.Outputs(y=base)
     # x NULL
     st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), None, C.byref(out),
-                               None, None, 0, None)
+                               None, None, 0, None, None)
     assert st == 1 and "x" in err(lib)
     # a misaligned weight
     w.gate = base + 2
     st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, C.byref(out),
-                               None, None, 0, None)
+                               None, None, 0, None, None)
     assert st == 3 and "gate" in err(lib)
     # NULL weights struct / outputs
     assert lib.q3l_layer_forward(C.byref(cfg), None, base, C.byref(out),
-                                 None, None, 0, None) == 1
+                                 None, None, 0, None, None) == 1
     w.gate = base
     assert lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, None,
-                                 None, None, 0, None) == 1
+                                 None, None, 0, None, None) == 1
 
 
 def test_backward_rejects_bad_flags_and_small_workspace(abi, lib):
@@ -167,15 +167,15 @@ def test_backward_rejects_bad_flags_and_small_workspace(abi, lib):
     w = abi.Weights(**{n: base for n in abi.PARAMS})
     g = abi.Grads(**{n: base for n in abi.PARAMS})
     st = lib.q3l_layer_backward(C.byref(cfg), C.byref(w), base, base, base, base,
-                                C.byref(g), 64, base, 1 << 40, None)
+                                C.byref(g), 64, base, 1 << 40, None, None)
     assert st == 1 and "flag" in err(lib)
     st = lib.q3l_layer_backward(C.byref(cfg), C.byref(w), base, base, base, base,
                                 C.byref(g), abi.BWD_INPUT | abi.BWD_WEIGHT,
-                                base, 16, None)
+                                base, 16, None, None)
     assert st == 1 and "workspace" in err(lib)
     tp = cfg_of(abi, tp_partial=1)
     st = lib.q3l_layer_backward(C.byref(tp), C.byref(w), base, base, base, base,
-                                C.byref(g), abi.BWD_INPUT, base, 1 << 40, None)
+                                C.byref(g), abi.BWD_INPUT, base, 1 << 40, None, None)
     assert st == 2
 
 
@@ -208,8 +208,8 @@ def test_attention_offset_range_is_checked(abi, lib):
     assert st == 2 and "2 GiB" in err(lib)
     ws = lib.q3l_attention_bwd_workspace_bytes(1, L, hq)
     st = lib.q3l_attention_bwd(abi.Q3L_BF16, 1, L, hq, hkv, dh, p, hq * dh, p,
-                               hkv * dh, p, hkv * dh, p, p, hq * dh, p, p, p, p, p,
-                               ws, None)
+                               hkv * dh, p, hkv * dh, p, hq * dh, p, hq * dh, p, p,
+                               p, p, p, ws, None)
     assert st == 2 and "2 GiB" in err(lib)
 
 
@@ -219,3 +219,114 @@ def test_version_and_missing_library_fails_loudly(abi, lib, monkeypatch):
     monkeypatch.setattr(abi, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         abi.load("/nonexistent/libq3layer.so")
+
+
+def _host_bufs(abi):
+    buf = C.create_string_buffer(8192)
+    base = (C.addressof(buf) + 255) // 256 * 256
+    return buf, base
+
+
+def test_deferred_weight_flag_rules(abi, lib):
+    # DEFERRED_WEIGHT only goes with WEIGHT and without INPUT; the check
+    # comes before any launch.
+    cfg = cfg_of(abi)
+    buf, base = _host_bufs(abi)
+    w = abi.Weights(**{n: base for n in abi.PARAMS})
+    g = abi.Grads(**{n: base for n in abi.PARAMS})
+    for flags in (abi.BWD_DEFERRED_WEIGHT,
+                  abi.BWD_DEFERRED_WEIGHT | abi.BWD_INPUT | abi.BWD_WEIGHT,
+                  abi.BWD_DEFERRED_WEIGHT | abi.BWD_INPUT):
+        st = lib.q3l_layer_backward(C.byref(cfg), C.byref(w), base, base, base, base,
+                                    C.byref(g), flags, base, 1 << 40, None, None)
+        assert st == 1 and "DEFERRED" in err(lib), flags
+
+
+def test_exec_marks_are_checked(abi, lib):
+    # A marks array must hold phase_count + 1 events; a side stream needs its
+    # two events.  All rejected before anything is enqueued.
+    assert lib.q3l_phase_count(0) >= 8 and lib.q3l_phase_count(1) >= 13
+    names = [lib.q3l_phase_name(1, i).decode() for i in range(lib.q3l_phase_count(1))]
+    assert any("attention" in n for n in names) and len(set(names)) == len(names)
+    assert lib.q3l_phase_name(0, lib.q3l_phase_count(0)) is None
+    assert lib.q3l_phase_name(0, -1) is None
+    cfg = cfg_of(abi)
+    buf, base = _host_bufs(abi)
+    w = abi.Weights(**{n: base for n in abi.PARAMS})
+    out = abi.Outputs(y=base)
+    arr = (C.c_void_p * 3)(base, base, base)
+    ex = abi.Exec(marks=C.cast(arr, C.POINTER(C.c_void_p)), n_marks=3)
+    st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, C.byref(out), base,
+                               None, 0, None, C.byref(ex))
+    assert st == 1 and "n_marks" in err(lib)
+    ex = abi.Exec(n_marks=2)
+    st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, C.byref(out), base,
+                               None, 0, None, C.byref(ex))
+    assert st == 1 and "marks" in err(lib)
+    ex = abi.Exec(side_stream=base)
+    st = lib.q3l_layer_forward(C.byref(cfg), C.byref(w), base, C.byref(out), base,
+                               None, 0, None, C.byref(ex))
+    assert st == 1 and "fork_event" in err(lib)
+
+
+def test_tp_share_saves_no_transposed_copies(abi, lib):
+    # The forward-only tensor-parallel share has no backward: its saved block
+    # ends before the transposed copies a backward would read.
+    cfg = cfg_of(abi, tp_partial=1)
+    lay = abi.SavedLayout()
+    assert lib.q3l_saved_layout_of(C.byref(cfg), C.byref(lay)) == 0
+    assert lay.wt == lay.xnt == lay.total
+    full = abi.SavedLayout()
+    cfg2 = cfg_of(abi)
+    assert lib.q3l_saved_layout_of(C.byref(cfg2), C.byref(full)) == 0
+    assert full.xnt > full.wt and full.total > full.xnt
+
+
+def test_linear_calls_reject_operands_past_the_32bit_offset_range(abi, lib):
+    # bf16 GEMM operands are addressed with 32-bit byte offsets: an activation
+    # or weight of 2 GiB or more is refused before any launch; fp32 is not.
+    buf, base = _host_bufs(abi)
+    M, N, K = 1 << 20, 1024, 1024          # [M, K] bf16 activation = 2 GiB
+    st = lib.q3l_linear_fwd(abi.Q3L_BF16, M, N, K, base, base, None, base, None)
+    assert st == 2 and "2 GiB" in err(lib)
+    st = lib.q3l_linear_dgrad(abi.Q3L_BF16, 16, 1 << 17, 1 << 13, base, base, base, None)
+    assert st == 2 and "2 GiB" in err(lib)
+    st = lib.q3l_linear_wgrad(abi.Q3L_BF16, M, N, K, base, base, base, 0, None)
+    assert st == 2
+    st = lib.q3l_swiglu_fwd(abi.Q3L_BF16, M // 2, N, K, base, base, base, base, None, None)
+    assert st == 2
+
+
+def test_new_phase_entries_validate(abi, lib):
+    buf, base = _host_bufs(abi)
+    # RMSNorm backward: width rules and workspace size.
+    assert lib.q3l_rmsnorm_bwd_workspace_bytes(4096) >= 4096 * 4
+    st = lib.q3l_rmsnorm_bwd(abi.Q3L_BF16, 4, 8200, base, base, base, base, None, base,
+                             base, 0, base, 1 << 30, None)
+    assert st == 2
+    st = lib.q3l_rmsnorm_bwd(abi.Q3L_BF16, 4, 512, base, base, base, base, None, base,
+                             base, 0, base, 16, None)
+    assert st == 1 and "workspace" in err(lib)
+    st = lib.q3l_rmsnorm_bwd(abi.Q3L_BF16, 4, 512, base, base, base, base, base + 2, base,
+                             base, 0, base, 1 << 30, None)
+    assert st == 3
+    # q/k norm + RoPE: head dim and strides.
+    st = lib.q3l_qknorm_rope_fwd(abi.Q3L_BF16, 1, 8, 4, 2, 96, 1, 1e-6, base, 576, base,
+                                 base, base, base, base, 576, base, base, None)
+    assert st == 2
+    st = lib.q3l_qknorm_rope_fwd(abi.Q3L_BF16, 1, 8, 4, 2, 64, 1, 1e-6, base, 100, base,
+                                 base, base, base, base, 384, base, base, None)
+    assert st == 1 and "stride" in err(lib)
+    ws = lib.q3l_qknorm_rope_bwd_workspace_bytes(64)
+    assert ws > 0 and lib.q3l_qknorm_rope_bwd_workspace_bytes(96) == 0
+    st = lib.q3l_qknorm_rope_bwd(abi.Q3L_BF16, 1, 8, 4, 2, 64, 1, base, 384, base, 384,
+                                 base, base, base, base, base, base, base, 384, base, None,
+                                 0, base, ws, None)
+    assert st == 1 and "dwq" in err(lib)
+    st = lib.q3l_rope_table(0, 64, 1e6, base, base, None)
+    assert st == 1
+    # SwiGLU adjoint: width and aliasing.
+    st = lib.q3l_swiglu_bwd(abi.Q3L_BF16, 16, 12, base, base, base + 256, None)
+    assert st == 1
+    st = lib.q3l_swiglu_bwd(abi.Q3L_BF16, 16, 16, base, base, base, None)
+    assert st == 1 and "alias" in err(lib)
