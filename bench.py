@@ -160,7 +160,7 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
     nf, nb = len(q3.phase_names(False)), len(q3.phase_names(True))
 
     def marks(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        return q3.MarkEvents(n + 1)
 
     def step(exf=side, exb=None):
         q3.layer_forward(lc, W, x, out=out, saved=saved, workspace=fwd_ws, stream=stream,
@@ -264,6 +264,45 @@ def kernel_probe(cfg: dict) -> None:
           flush=True)
 
 
+def split_probe(cfg: dict) -> None:
+    """One training forward, then the backward split in two calls: INPUT
+    (dx; leaves the activation gradients in the workspace) and WEIGHT |
+    DEFERRED_WEIGHT (the weight gradients only), each timed with HIP events
+    and followed by a device synchronisation, so that a kernel trace of this
+    run shows which kernels each call launches.  Prints one JSON line."""
+    import torch
+    import qwen3_decoder_layer_amd as q3
+    lc = q3.LayerConfig.from_dict(cfg)
+    inp = synth.make_inputs(cfg, 1000 + 4, with_dy=True)
+    W = {n: torch.from_numpy(inp[n]).to("cuda", torch.bfloat16) for n in synth.PARAM_NAMES}
+    x = torch.from_numpy(inp["x"]).to("cuda", torch.bfloat16)
+    dy = torch.from_numpy(inp["dy"]).to("cuda", torch.bfloat16)
+    saved = torch.empty(q3.saved_bytes(lc), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(q3.workspace_bytes(lc, True), dtype=torch.uint8, device="cuda")
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty(W[n].shape, dtype=torch.float32, device="cuda") for n in W}
+    calls = [("forward", lambda: q3.layer_forward(lc, W, x, saved=saved)),
+             ("backward INPUT", lambda: q3.layer_backward(
+                 lc, W, x, dy, saved, dx=dx, flags=q3.BWD_INPUT, workspace=ws)),
+             ("backward WEIGHT|DEFERRED_WEIGHT", lambda: q3.layer_backward(
+                 lc, W, x, dy, saved, grads=grads,
+                 flags=q3.BWD_WEIGHT | q3.BWD_DEFERRED_WEIGHT, workspace=ws)),
+             ("backward INPUT|WEIGHT", lambda: q3.layer_backward(
+                 lc, W, x, dy, saved, dx=dx, grads=grads, workspace=ws))]
+    for _, fn in calls:          # warm-up
+        fn()
+    torch.cuda.synchronize()
+    times = {}
+    for name, fn in calls:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times[name] = a.elapsed_time(b)
+    print(json.dumps({"workload": cfg["name"], "ms": times}), flush=True)
+
+
 def kernel_source_digest() -> str:
     """Digest of the dominant kernel's device code: gemm_bf16.hip and the
     helpers it includes (common.h), comments and whitespace removed, so a
@@ -326,6 +365,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the oracle sample (0: no CPU baseline)")
+    ap.add_argument("--split-probe", action="store_true",
+                    help="one forward and the backward as INPUT then "
+                         "WEIGHT|DEFERRED_WEIGHT calls (for a kernel trace)")
     ap.add_argument("--kernel-probe", action="store_true",
                     help="only the calibration copy and the dominant kernel "
                          "(for hardware-counter passes)")
@@ -337,6 +379,9 @@ def main():
               "supported (the layer's local compute runs on a single device).",
               file=sys.stderr)
         sys.exit(2)
+    if args.split_probe:
+        split_probe(synth.preset(WORKLOADS[args.workload]))
+        return
     if args.kernel_probe:
         kernel_probe(synth.preset(WORKLOADS[args.workload]))
         return
@@ -351,6 +396,8 @@ def main():
     for times, work in ((res["fwd_phase_ms"], fwd_work), (res["bwd_phase_ms"], bwd_work)):
         for name, t in times.items():
             bound, amount = work[name]
+            if name == "transposes for the backward" and cfg["backward"]:
+                continue   # on the second stream, beside F5: no time of its own
             if amount == 0 or t <= 0:
                 continue
             if bound == "mfma":

@@ -17,7 +17,7 @@ from . import _abi
 from ._abi import (BWD_ACCUMULATE, BWD_DEFERRED_WEIGHT, BWD_INPUT, BWD_WEIGHT,
                    PARAMS, Q3L_BF16, Q3L_F32)
 
-__all__ = ["LayerConfig", "Q3LError", "Exec", "validate", "saved_bytes",
+__all__ = ["LayerConfig", "Q3LError", "Exec", "MarkEvents", "validate", "saved_bytes",
            "workspace_bytes", "saved_layout", "phase_names", "layer_forward",
            "layer_backward", "rmsnorm_fwd", "rmsnorm_bwd", "rope_table",
            "qknorm_rope_fwd", "qknorm_rope_bwd", "linear_fwd", "linear_dgrad",
@@ -129,27 +129,85 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
+_HIP = None
+_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+
+def _hip():
+    """The HIP runtime already loaded into the process (torch's; the library
+    links against the same soname, so there is one runtime)."""
+    global _HIP
+    if _HIP is None:
+        h = C.CDLL("libamdhip64.so.7")
+        h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        h.hipEventDestroy.argtypes = [C.c_void_p]
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        h.hipEventSynchronize.argtypes = [C.c_void_p]
+        _HIP = h
+    return _HIP
+
+
+class MarkEvents:
+    """n timing events for phase marks, created with
+    hipEventDisableSystemFence: recording one costs no system-scope cache
+    writeback, so marks between kernels change the timed work little.
+    Read the times after the work has finished (elapsed())."""
+
+    def __init__(self, n):
+        import torch
+        torch.cuda.init()
+        hip = _hip()
+        self.handles = []
+        for _ in range(n):
+            e = C.c_void_p()
+            st = hip.hipEventCreateWithFlags(C.byref(e), _EVENT_DISABLE_SYSTEM_FENCE)
+            if st != 0:
+                raise Q3LError(f"hipEventCreateWithFlags failed ({st})")
+            self.handles.append(e.value)
+
+    def __len__(self):
+        return len(self.handles)
+
+    def elapsed(self, i, j):
+        hip = _hip()
+        if hip.hipEventSynchronize(self.handles[j]) != 0:
+            raise Q3LError("hipEventSynchronize failed")
+        ms = C.c_float()
+        if hip.hipEventElapsedTime(C.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise Q3LError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            hip = _hip()
+            for h in self.handles:
+                hip.hipEventDestroy(h)
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+
 class Exec:
     """Execution options of layer_forward / layer_backward (q3l_exec).
 
     side_stream: a torch.cuda.Stream for the bf16 training forward's
     transposed copies (run beside the attention step; two events for the
-    fork and join are created here).  marks: a list of
-    ``phase_count + 1`` timing events (``torch.cuda.Event(enable_timing=
-    True)``), recorded by the library at the phase boundaries; read them back
-    with ``phase_times()`` after synchronising."""
+    fork and join are created here).  marks: ``phase_count + 1`` timing
+    events -- a MarkEvents, or a list of ``torch.cuda.Event(enable_timing=
+    True)`` -- recorded by the library at the phase boundaries; read them
+    back with ``phase_times()``."""
 
     def __init__(self, side_stream=None, marks=None):
         import torch
         self.side_stream = side_stream
-        self.marks = list(marks) if marks else None
+        self.marks = marks if isinstance(marks, MarkEvents) else (
+            list(marks) if marks else None)
         self._fork = self._join = None
         if side_stream is not None:
             self._fork, self._join = torch.cuda.Event(), torch.cuda.Event()
             # torch creates the HIP event on its first record.
             for e in (self._fork, self._join):
                 e.record(side_stream)
-        if self.marks:
+        if self.marks and not isinstance(self.marks, MarkEvents):
             for e in self.marks:
                 e.record()
         self._arr = None
@@ -161,14 +219,17 @@ class Exec:
             ex.fork_event = self._fork.cuda_event
             ex.join_event = self._join.cuda_event
         if self.marks:
-            self._arr = (C.c_void_p * len(self.marks))(
-                *[e.cuda_event for e in self.marks])
+            hs = (self.marks.handles if isinstance(self.marks, MarkEvents)
+                  else [e.cuda_event for e in self.marks])
+            self._arr = (C.c_void_p * len(hs))(*hs)
             ex.marks = C.cast(self._arr, C.POINTER(C.c_void_p))
             ex.n_marks = len(self.marks)
         return ex
 
     def phase_times(self):
         """Milliseconds of each phase from the last call's marks."""
+        if isinstance(self.marks, MarkEvents):
+            return [self.marks.elapsed(i, i + 1) for i in range(len(self.marks) - 1)]
         return [a.elapsed_time(b) for a, b in zip(self.marks, self.marks[1:])]
 
 
