@@ -23,7 +23,9 @@
  * ---------------------------------------
  *  - All tensor arguments are DEVICE pointers to caller-owned memory; the
  *    library never allocates device memory, never synchronises, holds no
- *    mutable global state and keeps no pointer after a call returns.  Work is
+ *    mutable global state (one exception: the fixed scratch array of
+ *    q3l_attention_bwd_noalloc, at the end) and keeps no pointer after a
+ *    call returns.  Work is
  *    enqueued on `stream`, a hipStream_t passed as void* (NULL = the null
  *    stream).  Calls on distinct buffers may run from several host threads.
  *  - Layouts are dense row-major.  Activations are [B, L, features] = [T, .]
@@ -379,6 +381,26 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L,
                              int64_t lddo, const float *lse, void *dq,
                              void *dk, void *dv, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* q3l_attention_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace.  The row-sum scratch
+ * comes from a fixed device array inside the library, one per GPU, held
+ * until the process ends: B*h_q*L may not exceed
+ * q3l_attention_bwd_noalloc_max_rows() (4,194,304; Q3L_EINVAL beyond, before
+ * anything is enqueued).  The call allocates nothing.  All calls on one GPU
+ * share that array, so calls that overlap on one GPU (concurrent streams or
+ * host threads) race and must be serialised by the caller; results are
+ * bitwise those of q3l_attention_bwd. */
+size_t q3l_attention_bwd_noalloc_max_rows(void);
+q3l_status q3l_attention_bwd_noalloc(int32_t dtype, int32_t B, int32_t L,
+                                     int32_t h_q, int32_t h_kv, int32_t d_h,
+                                     const void *q, int64_t ldq, const void *k,
+                                     int64_t ldk, const void *v, int64_t ldv,
+                                     const void *o, int64_t ldo,
+                                     const void *dout, int64_t lddo,
+                                     const float *lse, void *dq, void *dk,
+                                     void *dv, void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ __all__ = ["LayerConfig", "Q3LError", "Exec", "MarkEvents", "validate", "saved_b
            "layer_backward", "rmsnorm_fwd", "rmsnorm_bwd", "rope_table",
            "qknorm_rope_fwd", "qknorm_rope_bwd", "linear_fwd", "linear_dgrad",
            "linear_wgrad", "swiglu_fwd", "swiglu_bwd", "attention_fwd",
-           "attention_bwd", "library", "param_shapes", "PARAMS", "BWD_INPUT",
+           "attention_bwd", "attention_bwd_noalloc", "library", "param_shapes", "PARAMS", "BWD_INPUT",
            "BWD_WEIGHT", "BWD_ACCUMULATE", "BWD_DEFERRED_WEIGHT"]
 
 
@@ -580,4 +580,19 @@ def attention_bwd(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq=None, dk=None,
         k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(dout),
         dout.stride(1), _p(lse), _p(dq), _p(dk), _p(dv), _p(ws), n,
         _stream(stream)))
+    return dq, dk, dv
+
+
+def attention_bwd_noalloc(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq, dk, dv, stream=None):
+    """q3l_attention_bwd_noalloc: the attention backward with the library's
+    built-in scratch; the caller passes every output (nothing is allocated
+    here or in the library)."""
+    B, L = q.shape[0], q.shape[1]
+    for a, b, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if a is None or a.stride() != b.stride() or a.shape != b.shape:
+            raise ValueError(f"{name} must be given with the shape and strides of its input")
+    _check(library().q3l_attention_bwd_noalloc(
+        _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k),
+        k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(dout),
+        dout.stride(1), _p(lse), _p(dq), _p(dk), _p(dv), _stream(stream)))
     return dq, dk, dv

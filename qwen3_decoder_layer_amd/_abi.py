@@ -100,6 +100,11 @@ PROTOTYPES = {
                                     _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                     _vp, _vp]),
     "q3l_attention_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "q3l_attention_bwd_noalloc_max_rows": (_sz, []),
+    "q3l_attention_bwd_noalloc": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                            _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                            _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                            _vp]),
     "q3l_attention_bwd": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _vp,
                                     _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                     _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz,

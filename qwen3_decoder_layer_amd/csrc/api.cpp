@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <cstring>
 #include <string>
 
@@ -1147,3 +1148,57 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The attention backward without caller-provided scratch.  Its one scratch
+// buffer (the row sums D = rowsum(dO * O), [B, h_q, L] fp32) lives in a
+// file-scope device array of fixed size instead; every GPU the library runs
+// on holds its own copy until the process ends.  Host code uses the array's
+// device address, taken once per device with hipGetSymbolAddress (the
+// array's name on the host is only a stand-in).  Nothing in it has to start
+// at zero: the dQ kernel writes every row sum the dK/dV kernel then reads.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchFloats = size_t(1) << 22;   // 16 MiB: B*h_q*L <= 4M
+__device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's address of `scratch` (taken on the first call on
+// that device; a race between two first calls stores the same address).
+q3l_status scratch_address(void** out) {
+  int dev = 0;
+  Q3L_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(Q3L_EUNSUPPORTED, "device %d beyond the %d this build tracks", dev,
+                kMaxScratchDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    Q3L_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(Q3L_EHIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return Q3L_OK;
+}
+}  // namespace
+
+extern "C" size_t q3l_attention_bwd_noalloc_max_rows(void) { return kScratchFloats; }
+
+extern "C" q3l_status q3l_attention_bwd_noalloc(
+    int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv, int32_t d_h, const void* q,
+    int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv, const void* o,
+    int64_t ldo, const void* dout, int64_t lddo, const float* lse, void* dq, void* dk, void* dv,
+    void* stream) {
+  q3l_status st = check_attn(dtype, B, L, h_q, h_kv, d_h);
+  if (st != Q3L_OK) return st;
+  if ((int64_t)B * h_q * L > (int64_t)kScratchFloats)
+    return fail(Q3L_EINVAL, "B*h_q*L = %lld exceeds the %zu row sums the built-in scratch "
+                "holds; use q3l_attention_bwd with a workspace",
+                (long long)B * h_q * L, kScratchFloats);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != Q3L_OK) return st;
+  return q3l_attention_bwd(dtype, B, L, h_q, h_kv, d_h, q, ldq, k, ldk, v, ldv, o, ldo, dout,
+                           lddo, lse, dq, dk, dv, ws, kScratchFloats * sizeof(float), stream);
+}
