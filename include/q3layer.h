@@ -366,6 +366,41 @@ q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L,
                              int64_t ldk, const void *v, int64_t ldv, void *o,
                              int64_t ldo, float *lse, void *stream);
 
+/* Attention over one block of keys, as the parallelism page's ring-attention
+ * section (4.2) builds it: for every sequence b, q head j and query t, over
+ * the keys s in [k0, k1) with s <= t (positions within the sequence; the
+ * causal rule of Step 5), with S = q k / sqrt(d_h):
+ *   m = max S (the block's largest score), l = sum exp(S - m),
+ *   acc = sum exp(S - m) v_s   (unnormalised, fp32),
+ * and (-inf, 0, 0) for a query that sees no key of the block.  q, k, v as
+ * for q3l_attention_fwd; m, l [B, h_q, L] fp32; acc [B*L, h_q*d_h] fp32
+ * (dense).  0 <= k0 < k1 <= L.  States of disjoint key blocks combine with
+ * q3l_attention_merge, in any order, to the state of their union; the
+ * merged state of a partition of [0, L) gives the attention output through
+ * q3l_attention_finish. */
+q3l_status q3l_attention_fwd_block(int32_t dtype, int32_t B, int32_t L,
+                                   int32_t h_q, int32_t h_kv, int32_t d_h,
+                                   const void *q, int64_t ldq, const void *k,
+                                   int64_t ldk, const void *v, int64_t ldv,
+                                   int32_t k0, int32_t k1, float *m, float *l,
+                                   float *acc, void *stream);
+
+/* The merge rule of the same section, in place: with m_new = max(m, m2),
+ * l = l e^(m - m_new) + l2 e^(m2 - m_new), acc likewise, m = m_new (a
+ * (-inf, 0, 0) state drops out).  Layouts as q3l_attention_fwd_block. */
+q3l_status q3l_attention_merge(int32_t B, int32_t L, int32_t h_q, int32_t d_h,
+                               float *m, float *l, float *acc, const float *m2,
+                               const float *l2, const float *acc2,
+                               void *stream);
+
+/* The output of a (merged) state: o = acc / l (dtype, row stride ldo) and
+ * lse = m + log l (natural log, [B, h_q, L] fp32; -inf and o = 0 where l is
+ * 0). */
+q3l_status q3l_attention_finish(int32_t dtype, int32_t B, int32_t L,
+                                int32_t h_q, int32_t d_h, const float *m,
+                                const float *l, const float *acc, void *o,
+                                int64_t ldo, float *lse, void *stream);
+
 /* Its backward: dq, dk, dv (dtype) are written with the row strides of q, k,
  * v (ldq, ldk, ldv) -- a caller that passes strided views must give dq, dk,
  * dv buffers of the same strides -- from o (stride ldo), dout (stride

@@ -33,7 +33,8 @@ from .layer import (rmsnorm, rmsnorm_backward, linear, linear_backward,
                     layer_forward_rows)
 from .accounting import (param_counts, param_total, megatron_layer_params,
                          megatron_model_params)
-from .online_softmax import block_state, merge_states, finish_state
+from .online_softmax import (block_state, merge_states, finish_state,
+                             attention_block_state, merge_block_states)
 
 __all__ = [
     "rmsnorm", "rmsnorm_backward", "linear", "linear_backward",
@@ -42,5 +43,6 @@ __all__ = [
     "swiglu_backward", "layer_forward", "layer_backward",
     "layer_forward_rows", "param_counts", "param_total",
     "megatron_layer_params", "megatron_model_params", "block_state",
-    "merge_states", "finish_state",
+    "merge_states", "finish_state", "attention_block_state",
+    "merge_block_states",
 ]

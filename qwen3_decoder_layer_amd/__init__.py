@@ -22,7 +22,8 @@ __all__ = ["LayerConfig", "Q3LError", "Exec", "MarkEvents", "validate", "saved_b
            "layer_backward", "rmsnorm_fwd", "rmsnorm_bwd", "rope_table",
            "qknorm_rope_fwd", "qknorm_rope_bwd", "linear_fwd", "linear_dgrad",
            "linear_wgrad", "swiglu_fwd", "swiglu_bwd", "attention_fwd",
-           "attention_bwd", "attention_bwd_noalloc", "library", "param_shapes", "PARAMS", "BWD_INPUT",
+           "attention_bwd", "attention_bwd_noalloc", "attention_fwd_block",
+           "attention_merge", "attention_finish", "library", "param_shapes", "PARAMS", "BWD_INPUT",
            "BWD_WEIGHT", "BWD_ACCUMULATE", "BWD_DEFERRED_WEIGHT"]
 
 
@@ -551,6 +552,51 @@ def attention_fwd(q, k, v, h_q, h_kv, d_h, o=None, lse=None, stream=None):
         _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k),
         k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(lse),
         _stream(stream)))
+    return o, lse
+
+
+def attention_fwd_block(q, k, v, h_q, h_kv, d_h, k0, k1, m=None, l=None, acc=None,
+                        stream=None):
+    """Block state (m, l, acc) of attention over keys [k0, k1) (fp32)."""
+    import torch
+    B, L = q.shape[0], q.shape[1]
+    m = torch.empty((B, h_q, L), dtype=torch.float32, device=q.device) if m is None else m
+    l = torch.empty((B, h_q, L), dtype=torch.float32, device=q.device) if l is None else l
+    acc = (torch.empty((B, L, h_q * d_h), dtype=torch.float32, device=q.device)
+           if acc is None else acc)
+    for t, name, n in ((m, "m", B * h_q * L), (l, "l", B * h_q * L),
+                       (acc, "acc", B * L * h_q * d_h)):
+        _need(t, name, numel=n, dtype=torch.float32)
+    _check(library().q3l_attention_fwd_block(
+        _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k), k.stride(1),
+        _p(v), v.stride(1), int(k0), int(k1), _p(m), _p(l), _p(acc), _stream(stream)))
+    return m, l, acc
+
+
+def attention_merge(state, state2, stream=None):
+    """state := merge(state, state2) in place; states are (m, l, acc)."""
+    m, l, acc = state
+    m2, l2, acc2 = state2
+    B, h_q, L = m.shape
+    d_h = acc.shape[-1] // h_q
+    for a, b, name in ((m2, m, "m2"), (l2, l, "l2"), (acc2, acc, "acc2")):
+        _need(a, name, numel=b.numel(), dtype=b.dtype)
+    _check(library().q3l_attention_merge(B, L, h_q, d_h, _p(m), _p(l), _p(acc), _p(m2),
+                                         _p(l2), _p(acc2), _stream(stream)))
+    return state
+
+
+def attention_finish(state, dtype="bf16", o=None, lse=None, stream=None):
+    """(o, lse) of a merged state."""
+    import torch
+    m, l, acc = state
+    B, h_q, L = m.shape
+    d_h = acc.shape[-1] // h_q
+    td = torch.bfloat16 if _code(dtype) == Q3L_BF16 else torch.float32
+    o = torch.empty((B, L, h_q * d_h), dtype=td, device=m.device) if o is None else o
+    lse = torch.empty((B, h_q, L), dtype=torch.float32, device=m.device) if lse is None else lse
+    _check(library().q3l_attention_finish(_code(dtype), B, L, h_q, d_h, _p(m), _p(l), _p(acc),
+                                          _p(o), o.stride(1), _p(lse), _stream(stream)))
     return o, lse
 
 

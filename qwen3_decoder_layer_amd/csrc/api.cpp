@@ -1110,6 +1110,57 @@ q3l_status q3l_attention_fwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   return Q3L_OK;
 }
 
+q3l_status q3l_attention_fwd_block(int32_t dtype, int32_t B, int32_t L, int32_t h_q,
+                                   int32_t h_kv, int32_t d_h, const void* q, int64_t ldq,
+                                   const void* k, int64_t ldk, const void* v, int64_t ldv,
+                                   int32_t k0, int32_t k1, float* m, float* l, float* acc,
+                                   void* stream) {
+  q3l_status st = check_attn(dtype, B, L, h_q, h_kv, d_h);
+  if (st != Q3L_OK) return st;
+  if (k0 < 0 || k1 <= k0 || k1 > L)
+    return fail(Q3L_EINVAL, "key range [%d, %d) must satisfy 0 <= k0 < k1 <= L=%d", k0, k1, L);
+  Q3L_CHECK_PTR(q, "q"); Q3L_CHECK_PTR(k, "k"); Q3L_CHECK_PTR(v, "v");
+  Q3L_CHECK_PTR(m, "m"); Q3L_CHECK_PTR(l, "l"); Q3L_CHECK_PTR(acc, "acc");
+  if (ldq < (int64_t)h_q * d_h || ldk < (int64_t)h_kv * d_h || ldv < (int64_t)h_kv * d_h ||
+      ldq % 8 || ldk % 8 || ldv % 8)
+    return fail(Q3L_EINVAL, "row strides too small or not multiples of 8");
+  if ((st = check_attn_range(dtype, B, L, h_q, std::max(std::max(ldq, ldk), ldv))) != Q3L_OK)
+    return st;
+  AttnArgs a{};
+  a.B = B; a.L = L; a.h_q = h_q; a.h_kv = h_kv; a.d_h = d_h;
+  a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.v = v; a.ldv = ldv;
+  a.k_lo = k0; a.k_hi = k1;
+  a.m_out = m; a.l_out = l; a.acc = acc; a.ld_acc = (int64_t)h_q * d_h;
+  Q3L_HIP(attn_block(dtype, a, static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
+q3l_status q3l_attention_merge(int32_t B, int32_t L, int32_t h_q, int32_t d_h, float* m,
+                               float* l, float* acc, const float* m2, const float* l2,
+                               const float* acc2, void* stream) {
+  if (B <= 0 || L <= 0 || h_q <= 0) return fail(Q3L_EINVAL, "need positive B, L, h_q");
+  if (d_h != 64 && d_h != 128) return fail(Q3L_EUNSUPPORTED, "d_h must be 64 or 128");
+  Q3L_CHECK_PTR(m, "m"); Q3L_CHECK_PTR(l, "l"); Q3L_CHECK_PTR(acc, "acc");
+  Q3L_CHECK_PTR(m2, "m2"); Q3L_CHECK_PTR(l2, "l2"); Q3L_CHECK_PTR(acc2, "acc2");
+  Q3L_HIP(attn_state_merge(B, L, h_q, d_h, m, l, acc, m2, l2, acc2,
+                           static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
+q3l_status q3l_attention_finish(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t d_h,
+                                const float* m, const float* l, const float* acc, void* o,
+                                int64_t ldo, float* lse, void* stream) {
+  if (dtype != Q3L_F32 && dtype != Q3L_BF16) return fail(Q3L_EINVAL, "bad dtype");
+  if (B <= 0 || L <= 0 || h_q <= 0) return fail(Q3L_EINVAL, "need positive B, L, h_q");
+  if (d_h != 64 && d_h != 128) return fail(Q3L_EUNSUPPORTED, "d_h must be 64 or 128");
+  if (ldo < (int64_t)h_q * d_h || ldo % 8) return fail(Q3L_EINVAL, "bad ldo");
+  Q3L_CHECK_PTR(m, "m"); Q3L_CHECK_PTR(l, "l"); Q3L_CHECK_PTR(acc, "acc");
+  Q3L_CHECK_PTR(o, "o"); Q3L_CHECK_PTR(lse, "lse");
+  Q3L_HIP(attn_state_finish(dtype, B, L, h_q, d_h, m, l, acc, o, ldo, lse,
+                            static_cast<hipStream_t>(stream)));
+  return Q3L_OK;
+}
+
 size_t q3l_attention_bwd_workspace_bytes(int32_t B, int32_t L, int32_t h_q) {
   if (B <= 0 || L <= 0 || h_q <= 0) return 0;
   return up((size_t)B * h_q * L * 4);

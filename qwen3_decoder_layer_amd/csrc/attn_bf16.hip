@@ -51,6 +51,9 @@ struct FwdP {
   const bf16_t* dout; int64_t lddo;
   bf16_t* dq; bf16_t* dk; bf16_t* dv;
   float* delta;   // written by the dQ kernel, read by dK/dV
+  // block state (forward over the keys [k_lo, k_hi) only; unnormalised)
+  int k_lo, k_hi;
+  float* m_out; float* l_out; float* acc; int64_t ld_acc;
 };
 
 __device__ inline u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
@@ -182,7 +185,12 @@ struct TrOffsets {
 };
 
 // ============================ forward =======================================
-template <int DH>
+// STATE: the block form -- only keys in [k_lo, k_hi) (and s <= t) count,
+// and the output is the unnormalised state of the parallelism page's
+// ring-attention merge: m = the largest scaled score (natural log), l = sum
+// of exp(score - m), acc = sum of exp(score - m) v (fp32); rows with no
+// visible key get (-inf, 0, 0).
+template <int DH, bool STATE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   constexpr int NKK = DH / 16;   // k-steps over the head dim
   constexpr int NDT = DH / 32;   // 32-row tiles of d
@@ -206,11 +214,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   const int L = p.L;
   const int64_t tok0 = (int64_t)b * L;
 
-  // K/V tiles needed by the workgroup and by this wave.
+  // K/V tiles needed by the workgroup and by this wave, counted from tile
+  // tb (0, or the first tile of the key range in the block form).
   const int qend = min(q0 + QB, L);
-  const int ntiles = (qend + KT - 1) / KT;
   const int wave_last = min(qw0 + 31, L - 1);
-  const int my_tiles = qw0 < L ? wave_last / KT + 1 : 0;
+  const int kend_g = STATE ? min(qend, p.k_hi) : qend;
+  const int kend_w = STATE ? min(wave_last + 1, p.k_hi) : wave_last + 1;
+  const int tb = STATE ? p.k_lo / KT : 0;
+  const int ntiles = (kend_g + KT - 1) / KT - tb;
+  const int my_tiles = qw0 < L ? (kend_w + KT - 1) / KT - tb : 0;
 
   // Q fragments (second MFMA operand: lane owns query row qw0 + l32).
   u32x4_t qf[NKK];
@@ -231,10 +243,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   auto kslot = [&](int s) { return lds + s * TB; };
   auto vslot = [&](int s) { return lds + (2 + s) * TB; };
   auto load_k = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, t * KT, L, kslot(s), wave, lane);
+    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, (tb + t) * KT, L, kslot(s), wave,
+                             lane);
   };
   auto load_v = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, t * KT, L, vslot(s), wave, lane);
+    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, (tb + t) * KT, L, vslot(s), wave,
+                             lane);
   };
   uint32_t offk[NKK];
   {
@@ -263,7 +277,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  float m_max = -INFINITY;   // block form: the exact row maximum (log2 units)
   const int qrow = qw0 + l32;
+
+  if constexpr (STATE) {
+    // No key of the range is visible to any row of the workgroup (uniform).
+    if (ntiles <= 0) {
+      if (qrow < L) {
+        float* ap = p.acc + (tok0 + qrow) * p.ld_acc + (int64_t)head * DH;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4_t*>(ap + 32 * dt + 8 * j + 4 * h) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (h == 0) {
+          const int64_t si = ((int64_t)b * p.h_q + head) * L + qrow;
+          p.m_out[si] = -INFINITY;
+          p.l_out[si] = 0.f;
+        }
+      }
+      return;
+    }
+  }
 
   load_k(0, 0);
   if (ntiles > 1) load_k(1, 1);
@@ -281,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     if (t + 1 < ntiles) load_v(t + 1, s ^ 1);
     if (t < my_tiles) {
       f32x16_t (&cur)[2] = sc[s];
-      const int kv0 = t * KT;
+      const int kv0 = (tb + t) * KT;
       // Row maximum; only tiles that reach the diagonal or the sequence end
       // mask.  The two cases are separate straight-line code paths.
       float mx = -INFINITY;
@@ -293,13 +328,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
             float v = cur[c][e];
             if constexpr (decltype(masked)::value) {
               const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-              v = (kv > qrow || kv >= L) ? -INFINITY : v;
+              bool out = kv > qrow || kv >= L;
+              if constexpr (STATE) out = out || kv < p.k_lo || kv >= p.k_hi;
+              v = out ? -INFINITY : v;
               cur[c][e] = v;
             }
             mx = fmaxf(mx, v);
           }
       };
-      if ((kv0 + KT - 1 > qw0) || (kv0 + KT > L))
+      bool edge = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
+      if constexpr (STATE) edge = edge || kv0 < p.k_lo || kv0 + KT > p.k_hi;
+      if (edge)
         row_max(std::true_type{});
       else
         row_max(std::false_type{});
@@ -310,12 +349,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
                                                         false, false);
         mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.scale_log2;   // log2 units
       }
+      if constexpr (STATE) m_max = fmaxf(m_max, mx);
       // The reference maximum m_run moves (and O, l are rescaled) only when a
       // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
       // the result is exact, and the 64-multiply rescale is usually skipped.
       if (__any(mx > m_run + kTau)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_raw(m_run - m_new);
+        // (Block form: a row with no visible key so far, beside rows that
+        // rescale, has m_run = m_new = -inf; its O and l are still zero.)
+        const float alpha = (STATE && m_new == -INFINITY) ? 0.f : exp2_raw(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
 #pragma unroll
@@ -326,7 +368,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
       // Scores of tile t+1 (unused past this wave's last tile: the slot then
       // holds another tile or stale data, which is harmless to read).
       scores(kslot(s ^ 1), sc[s ^ 1]);
-      const float neg = -m_run;
+      // (Block form: a row that has seen no visible key yet keeps m_run =
+      // -inf; its masked scores then give exp2(-inf) = 0, not NaN.)
+      const float neg = (STATE && m_run == -INFINITY) ? 0.f : -m_run;
       float rs = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -355,6 +399,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 
   l_run += __shfl_xor(l_run, 32, 64);
   if (qrow >= L) return;
+  if constexpr (STATE) {
+    // Rescale to the exact row maximum (m_run may trail it by up to kTau).
+    const bool none = m_max == -INFINITY;
+    const float a = none ? 0.f : exp2_raw(m_run - m_max);
+    float* ap = p.acc + (tok0 + qrow) * p.ld_acc + (int64_t)head * DH;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4_t*>(ap + 32 * dt + 8 * j + 4 * h) =
+            none ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                 : f32x4_t{oacc[dt][4 * j] * a, oacc[dt][4 * j + 1] * a,
+                           oacc[dt][4 * j + 2] * a, oacc[dt][4 * j + 3] * a};
+    if (h == 0) {
+      const int64_t si = ((int64_t)b * p.h_q + head) * L + qrow;
+      p.m_out[si] = none ? -INFINITY : m_max * kLn2;
+      p.l_out[si] = none ? 0.f : l_run * a;
+    }
+    return;
+  }
   const float inv = 1.0f / l_run;
   bf16_t* op = p.o + (tok0 + qrow) * p.ldo + (int64_t)head * DH;
 #pragma unroll
@@ -824,9 +888,23 @@ hipError_t attn_fwd_bf16(const AttnArgs& a, hipStream_t s) {
   const int QB = 32 * p.rb;
   dim3 grid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
   if (a.d_h == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t attn_block_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.L <= 0) return hipSuccess;
+  FwdP p = make_params(a);
+  p.k_lo = a.k_lo; p.k_hi = a.k_hi;
+  p.m_out = a.m_out; p.l_out = a.l_out; p.acc = a.acc; p.ld_acc = a.ld_acc;
+  const int QB = 32 * p.rb;
+  dim3 grid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
+  if (a.d_h == 128)
+    hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

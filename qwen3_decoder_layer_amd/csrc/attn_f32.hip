@@ -19,6 +19,8 @@ struct F32P {
   float* dq; float* dk; float* dv;
   float* delta;
   float scale;
+  int k_lo, k_hi;
+  float* m_out; float* l_out; float* acc; int64_t ld_acc;
 };
 
 // d_h <= 128: each lane owns elements lane and lane + 64.
@@ -58,6 +60,46 @@ __global__ void attn_fwd_f32_kernel(const F32P p) {
     if (d < p.d_h) orow[d] = acc[i] / l;
   }
   if (lane == 0) p.lse[((tok0 / p.L) * p.h_q + head) * p.L + t] = m + logf(l);
+}
+
+// Block state over keys [k_lo, min(k_hi, t + 1)): running maximum m (the
+// exact maximum at the end), l and the unnormalised acc, (-inf, 0, 0) for a
+// row with no visible key in the range.
+__global__ void attn_block_f32_kernel(const F32P p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)p.B * p.L * p.h_q) return;
+  const int head = (int)(item % p.h_q);
+  const int64_t tok = item / p.h_q;
+  const int t = (int)(tok % p.L);
+  const int64_t tok0 = tok - t;
+  const int kvh = head / (p.h_q / p.h_kv);
+  const float* qr = p.q + tok * p.ldq + (int64_t)head * p.d_h;
+  float m = -INFINITY, l = 0.f, acc[2] = {0.f, 0.f};
+  const int s_end = min(p.k_hi, t + 1);
+  for (int s = p.k_lo; s < s_end; ++s) {
+    const float* kr = p.k + (tok0 + s) * p.ldk + (int64_t)kvh * p.d_h;
+    const float* vr = p.v + (tok0 + s) * p.ldv + (int64_t)kvh * p.d_h;
+    const float sc = wdot(qr, kr, p.d_h, lane) * p.scale;
+    const float mn = fmaxf(m, sc);
+    const float a = expf(m - mn), w = expf(sc - mn);
+    l = l * a + w;
+    for (int i = 0; i < 2; ++i) {
+      const int d = lane + 64 * i;
+      if (d < p.d_h) acc[i] = acc[i] * a + w * vr[d];
+    }
+    m = mn;
+  }
+  float* arow = p.acc + tok * p.ld_acc + (int64_t)head * p.d_h;
+  for (int i = 0; i < 2; ++i) {
+    const int d = lane + 64 * i;
+    if (d < p.d_h) arow[d] = acc[i];
+  }
+  if (lane == 0) {
+    const int64_t si = ((tok0 / p.L) * p.h_q + head) * p.L + t;
+    p.m_out[si] = m;
+    p.l_out[si] = l;
+  }
 }
 
 // dQ and delta = rowsum(dO * O).
@@ -162,6 +204,19 @@ hipError_t attn_fwd(int dtype, const AttnArgs& a, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.L * a.h_q;
   hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256),
                      0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t attn_block_bf16(const AttnArgs& a, hipStream_t s);
+
+hipError_t attn_block(int dtype, const AttnArgs& a, hipStream_t s) {
+  if (dtype == 1) return attn_block_bf16(a, s);
+  if (a.B <= 0 || a.L <= 0) return hipSuccess;
+  F32P p = make_p(a);
+  p.k_lo = a.k_lo; p.k_hi = a.k_hi;
+  p.m_out = a.m_out; p.l_out = a.l_out; p.acc = a.acc; p.ld_acc = a.ld_acc;
+  const int64_t items = (int64_t)a.B * a.L * a.h_q;
+  hipLaunchKernelGGL(attn_block_f32_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -151,8 +151,21 @@ struct AttnArgs {
   const void* dout; int64_t lddo;
   void* dq; void* dk; void* dv;   // strides ldq / ldk / ldv
   float* delta;                   // [B, h_q, L] scratch
+  // block state only: keys [k_lo, k_hi); m, l [B, h_q, L]; acc [B*L, ld_acc]
+  int k_lo, k_hi;
+  float* m_out; float* l_out; float* acc; int64_t ld_acc;
 };
 hipError_t attn_fwd(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t attn_bwd(int dtype, const AttnArgs& a, hipStream_t s);
+// Unnormalised block state (m, l, acc) of attention over keys [k_lo, k_hi).
+hipError_t attn_block(int dtype, const AttnArgs& a, hipStream_t s);
+// state (m, l, acc) := merge(state, state2) (in place); rows [B*L], heads h_q.
+hipError_t attn_state_merge(int B, int L, int h_q, int d_h, float* m, float* l, float* acc,
+                            const float* m2, const float* l2, const float* acc2,
+                            hipStream_t s);
+// o = acc / l (dtype, row stride ldo), lse = m + log l.
+hipError_t attn_state_finish(int dtype, int B, int L, int h_q, int d_h, const float* m,
+                             const float* l, const float* acc, void* o, int64_t ldo,
+                             float* lse, hipStream_t s);
 
 }  // namespace q3l

@@ -176,3 +176,63 @@ def test_tp_toy_outputs_do_not_depend_on_reconstruction(a10):
     assert np.allclose(Y, [[7.0, 10.0]])
     dX, _ = oracle.linear_backward(np.array([[1.0, 2.0]]), X, A.T)
     assert np.allclose(dX, [[5.0, 11.0]])
+
+
+def _page_example_tensors():
+    """The page's four-key example as attention inputs: one sequence of 4
+    tokens, one head, d_h = 64; the query at position 3 scores the keys
+    [1, 0, 2, 0] (q = 8 e_0, k_s = score_s e_0, so q.k / sqrt(64) = score)
+    and the values are the printed 2-vectors padded with zeros."""
+    fx = _load("online_softmax_example.json")
+    scores = np.array(fx["scores_blocks"][0] + fx["scores_blocks"][1])
+    V = np.array(fx["values"])
+    L, dh = 4, 64
+    q = np.zeros((1, L, 1, dh)); q[0, :, 0, 0] = 8.0
+    k = np.zeros((1, L, 1, dh)); k[0, :, 0, 0] = scores
+    v = np.zeros((1, L, 1, dh)); v[0, :, 0, :2] = V
+    return fx, q, k, v
+
+
+def test_block_state_attention_on_the_page_example():
+    """Blocks [0, 2) and [2, 4) of the page's example through the per-query
+    block-state attention: the last query's states, merged, give the printed
+    output (1.000, 0.693) and merged l = 1.639."""
+    fx, q, k, v = _page_example_tensors()
+    tol = fx["print_precision"]
+    a = oracle.attention_block_state(q, k, v, 0, 2)
+    b = oracle.attention_block_state(q, k, v, 2, 4)
+    # Query 3's states are the page's two block states.
+    s1, s2 = fx["scores_blocks"]
+    V = np.array(fx["values"])
+    for st, (sc, vv) in ((a, (s1, V[:2])), (b, (s2, V[2:]))):
+        m_ref, l_ref, acc_ref = oracle.block_state(sc, vv)
+        assert st[0][0, 0, 3] == m_ref
+        assert abs(st[1][0, 0, 3] - l_ref) < 1e-14
+        assert np.allclose(st[2][0, 3, 0, :2], acc_ref, atol=1e-14)
+        assert not st[2][0, 3, 0, 2:].any()
+    m, l, acc = oracle.merge_block_states(a, b)
+    out = acc[0, 3, 0, :2] / l[0, 0, 3]
+    assert np.allclose(out, fx["printed"]["output"], atol=tol)
+    assert m[0, 0, 3] == 2.0 and abs(l[0, 0, 3] - fx["printed"]["merged_l"]) < tol
+    # Query 0 sees only key 0: block [2, 4) is empty for it.
+    assert b[0][0, 0, 0] == -np.inf and b[1][0, 0, 0] == 0.0 and not b[2][0, 0].any()
+
+
+@pytest.mark.parametrize("cuts", [[0, 131], [0, 37, 131], [0, 64, 65, 100, 131]])
+def test_block_states_merged_over_a_partition_equal_attention(cuts):
+    """Merging the block states of any partition of [0, L), in any order,
+    gives the one-pass softmax attention of the oracle (output and LSE)."""
+    rng = np.random.default_rng(len(cuts))
+    B, L, hq, hkv, dh = 2, 131, 4, 2, 64
+    q = rng.standard_normal((B, L, hq, dh))
+    k = rng.standard_normal((B, L, hkv, dh))
+    v = rng.standard_normal((B, L, hkv, dh))
+    O, LSE = oracle.attention(q, k, v)
+    states = [oracle.attention_block_state(q, k, v, a, b) for a, b in zip(cuts, cuts[1:])]
+    for order in (states, states[::-1]):
+        st = order[0]
+        for other in order[1:]:
+            st = oracle.merge_block_states(st, other)
+        m, l, acc = st
+        assert np.allclose(acc / np.transpose(l, (0, 2, 1))[..., None], O, rtol=1e-12, atol=1e-12)
+        assert np.allclose(m + np.log(l), LSE, rtol=1e-12, atol=1e-12)
