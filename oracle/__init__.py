@@ -33,6 +33,7 @@ from .layer import (rmsnorm, rmsnorm_backward, linear, linear_backward,
                     layer_forward_rows)
 from .accounting import (param_counts, param_total, megatron_layer_params,
                          megatron_model_params)
+from .model import model_forward, model_backward, model_param_counts
 from .online_softmax import (block_state, merge_states, finish_state,
                              attention_block_state, merge_block_states)
 
@@ -44,5 +45,6 @@ __all__ = [
     "layer_forward_rows", "param_counts", "param_total",
     "megatron_layer_params", "megatron_model_params", "block_state",
     "merge_states", "finish_state", "attention_block_state",
-    "merge_block_states",
+    "merge_block_states", "model_forward", "model_backward",
+    "model_param_counts",
 ]
