@@ -234,6 +234,74 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg *cfg, const q3l_weights *w,
                               void *workspace, size_t workspace_bytes,
                               void *stream, const q3l_exec *exec);
 
+/* ------------------------------------------------------------------------
+ * The model around a stack of layers (walkthrough page, "简化的 Qwen3 结构":
+ * embed_tokens [vocab, d], N_L decoder layers, a final RMSNorm, and an
+ * output projection tied to the embedding; hidden states flow from one
+ * layer into the next on the same device, the text after Steps 10-11):
+ *   x_0 = E[ids];  x_{i+1} = layer_i(x_i);  hf = RMSNorm(x_N; w_final);
+ *   logits = hf E^T.
+ * The loss is not part of the path: the backward starts from dlogits.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  q3l_layer_cfg layer; /* shapes and numerics of every layer (tp_partial 0) */
+  int32_t n_layers;    /* N_L >= 0                                         */
+  int32_t vocab;       /* V: rows of the embedding table, a multiple of 8  */
+  int32_t recompute;   /* 1: the forward keeps only each layer's input and
+                          the backward recomputes each layer's forward before
+                          its backward (the memory-model page's full
+                          recompute, section 3.3: one more forward, far less
+                          saved memory); 0: every layer's saved block is
+                          kept                                            */
+} q3l_model_cfg;
+
+typedef struct {
+  const void *embed;         /* [V, d] cfg dtype, also the output projection */
+  const void *final_norm;    /* [d] cfg dtype                               */
+  const q3l_weights *layers; /* host array of n_layers (device pointers)    */
+} q3l_model_weights;
+
+typedef struct {
+  float *embed;              /* [V, d] fp32: output projection + embedding  */
+  float *final_norm;         /* [d] fp32                                    */
+  const q3l_grads *layers;   /* host array of n_layers                      */
+} q3l_model_grads;
+
+/* Checks a model configuration (the layer's rules, V a positive multiple of
+ * 8, n_layers >= 0, B*L <= 262144 tokens, and in bf16 the logits and the
+ * table within the GEMM's 2 GiB offset range). */
+q3l_status q3l_model_validate(const q3l_model_cfg *cfg);
+/* Bytes of the `saved` buffer of a training forward (layer inputs, the
+ * final norm's output and statistics, and -- without recompute -- every
+ * layer's saved block); 0 if invalid. */
+size_t q3l_model_saved_bytes(const q3l_model_cfg *cfg);
+/* Bytes of scratch of q3l_model_forward (backward == 0) or
+ * q3l_model_backward (1); 0 if invalid. */
+size_t q3l_model_workspace_bytes(const q3l_model_cfg *cfg, int backward);
+
+/* Forward: ids [B*L] int32 device array (ids outside [0, V) embed as zero
+ * rows); logits [B*L, V] cfg dtype.  saved: NULL for inference, else
+ * q3l_model_saved_bytes(cfg) bytes kept for the backward.  exec: NULL, or
+ * options whose side_stream (and its events) each layer's forward uses;
+ * exec->marks must be NULL here. */
+q3l_status q3l_model_forward(const q3l_model_cfg *cfg,
+                             const q3l_model_weights *w, const int32_t *ids,
+                             void *logits, void *saved, void *workspace,
+                             size_t workspace_bytes, void *stream,
+                             const q3l_exec *exec);
+
+/* Backward from dlogits [B*L, V] (cfg dtype): every gradient of the stack,
+ * fp32, overwritten (flags 0) or added into (Q3L_BWD_ACCUMULATE).  The
+ * embedding table's gradient is the output projection's weight gradient
+ * plus, for every token, its row of dx_0 scattered into the token's row (in
+ * a fixed order: bitwise reproducible). */
+q3l_status q3l_model_backward(const q3l_model_cfg *cfg,
+                              const q3l_model_weights *w, const int32_t *ids,
+                              const void *dlogits, const void *saved,
+                              const q3l_model_grads *grads, int flags,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Thread-local text describing the last non-OK status ("" if none). */
 const char *q3l_last_error(void);
 

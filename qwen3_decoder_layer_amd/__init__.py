@@ -24,7 +24,9 @@ __all__ = ["LayerConfig", "Q3LError", "Exec", "MarkEvents", "validate", "saved_b
            "linear_wgrad", "swiglu_fwd", "swiglu_bwd", "attention_fwd",
            "attention_bwd", "attention_bwd_noalloc", "attention_fwd_block",
            "attention_merge", "attention_finish", "library", "param_shapes", "PARAMS", "BWD_INPUT",
-           "BWD_WEIGHT", "BWD_ACCUMULATE", "BWD_DEFERRED_WEIGHT"]
+           "BWD_WEIGHT", "BWD_ACCUMULATE", "BWD_DEFERRED_WEIGHT", "ModelConfig",
+           "model_validate", "model_saved_bytes", "model_workspace_bytes",
+           "model_forward", "model_backward"]
 
 
 class Q3LError(RuntimeError):
@@ -642,3 +644,101 @@ def attention_bwd_noalloc(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq, dk, dv, str
         k.stride(1), _p(v), v.stride(1), _p(o), o.stride(1), _p(dout),
         dout.stride(1), _p(lse), _p(dq), _p(dk), _p(dv), _stream(stream)))
     return dq, dk, dv
+
+
+# ---- the model around a stack of layers ----------------------------------
+@dataclass
+class ModelConfig:
+    layer: LayerConfig
+    n_layers: int
+    vocab: int
+    recompute: bool = False
+
+    def c_struct(self) -> _abi.ModelCfg:
+        return _abi.ModelCfg(self.layer.c_struct(), self.n_layers, self.vocab,
+                             int(bool(self.recompute)))
+
+
+def model_validate(mc: ModelConfig) -> None:
+    c = mc.c_struct()
+    _check(library().q3l_model_validate(C.byref(c)))
+
+
+def model_saved_bytes(mc: ModelConfig) -> int:
+    c = mc.c_struct()
+    return library().q3l_model_saved_bytes(C.byref(c))
+
+
+def model_workspace_bytes(mc: ModelConfig, backward: bool) -> int:
+    c = mc.c_struct()
+    return library().q3l_model_workspace_bytes(C.byref(c), int(bool(backward)))
+
+
+def _model_weights(mc: ModelConfig, embed, final_norm, layers):
+    cfg = mc.layer
+    _need(embed, "embed", numel=mc.vocab * cfg.d, dtype=cfg.torch_dtype)
+    _need(final_norm, "final_norm", numel=cfg.d, dtype=cfg.torch_dtype)
+    if len(layers) != mc.n_layers:
+        raise ValueError(f"{len(layers)} layer weight dicts for {mc.n_layers} layers")
+    arr = (_abi.Weights * max(1, mc.n_layers))(*[_weights(cfg, l) for l in layers])
+    return _abi.ModelWeights(embed.data_ptr(), final_norm.data_ptr(),
+                             C.cast(arr, C.POINTER(_abi.Weights))), arr
+
+
+def model_forward(mc: ModelConfig, embed, final_norm, layers, ids, logits=None,
+                  saved=None, workspace=None, stream=None, exec=None):
+    """q3l_model_forward: logits [B, L, V] of int32 token ids [B, L]."""
+    import torch
+    cfg = mc.layer
+    _need(ids, "ids", numel=cfg.T, dtype=torch.int32)
+    if logits is None:
+        logits = torch.empty((cfg.B, cfg.L, mc.vocab), dtype=cfg.torch_dtype, device=ids.device)
+    _need(logits, "logits", numel=cfg.T * mc.vocab, dtype=cfg.torch_dtype)
+    if saved is not None:
+        _need(saved, "saved", min_bytes=model_saved_bytes(mc))
+    if workspace is None:
+        workspace = _bytes(model_workspace_bytes(mc, False), ids.device)
+    w, keep = _model_weights(mc, embed, final_norm, layers)
+    c = mc.c_struct()
+    _check(library().q3l_model_forward(C.byref(c), C.byref(w), _p(ids), _p(logits), _p(saved),
+                                       _p(workspace), _nbytes(workspace), _stream(stream),
+                                       _exec(exec)))
+    del keep
+    return logits
+
+
+def model_backward(mc: ModelConfig, embed, final_norm, layers, ids, dlogits, saved,
+                   grads=None, accumulate=False, workspace=None, stream=None):
+    """q3l_model_backward: returns grads = {"embed", "final_norm", "layers":
+    [per-layer dicts]} (fp32)."""
+    import torch
+    cfg = mc.layer
+    dev = ids.device
+    _need(ids, "ids", numel=cfg.T, dtype=torch.int32)
+    _need(dlogits, "dlogits", numel=cfg.T * mc.vocab, dtype=cfg.torch_dtype)
+    _need(saved, "saved", min_bytes=model_saved_bytes(mc))
+    if grads is None:
+        grads = {"embed": torch.empty((mc.vocab, cfg.d), dtype=torch.float32, device=dev),
+                 "final_norm": torch.empty(cfg.d, dtype=torch.float32, device=dev),
+                 "layers": [{n: torch.empty(s, dtype=torch.float32, device=dev)
+                             for n, s in param_shapes(cfg).items()}
+                            for _ in range(mc.n_layers)]}
+    _need(grads["embed"], "grads['embed']", numel=mc.vocab * cfg.d, dtype=torch.float32)
+    _need(grads["final_norm"], "grads['final_norm']", numel=cfg.d, dtype=torch.float32)
+    garr = (_abi.Grads * max(1, mc.n_layers))(
+        *[_abi.Grads(*[g[n].data_ptr() for n in PARAMS]) for g in grads["layers"]])
+    for g in grads["layers"]:
+        for n, shp in param_shapes(cfg).items():
+            _need(g[n], f"grads[layers][{n!r}]", numel=int(__import__("math").prod(shp)),
+                  dtype=torch.float32)
+    mg = _abi.ModelGrads(grads["embed"].data_ptr(), grads["final_norm"].data_ptr(),
+                         C.cast(garr, C.POINTER(_abi.Grads)))
+    if workspace is None:
+        workspace = _bytes(model_workspace_bytes(mc, True), dev)
+    w, keep = _model_weights(mc, embed, final_norm, layers)
+    c = mc.c_struct()
+    _check(library().q3l_model_backward(C.byref(c), C.byref(w), _p(ids), _p(dlogits), _p(saved),
+                                        C.byref(mg), BWD_ACCUMULATE if accumulate else 0,
+                                        _p(workspace), _nbytes(workspace), _stream(stream)))
+    del keep
+    return grads

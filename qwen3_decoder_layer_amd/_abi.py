@@ -50,6 +50,21 @@ class SavedLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in SAVED_FIELDS]
 
 
+class ModelCfg(C.Structure):
+    _fields_ = [("layer", Cfg), ("n_layers", C.c_int32), ("vocab", C.c_int32),
+                ("recompute", C.c_int32)]
+
+
+class ModelWeights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p),
+                ("layers", C.POINTER(Weights))]
+
+
+class ModelGrads(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p),
+                ("layers", C.POINTER(Grads))]
+
+
 class Exec(C.Structure):
     _fields_ = [("side_stream", C.c_void_p), ("fork_event", C.c_void_p),
                 ("join_event", C.c_void_p), ("marks", C.POINTER(C.c_void_p)),
@@ -71,6 +86,14 @@ PROTOTYPES = {
                                      _vp, _sz, _vp, C.POINTER(Exec)]),
     "q3l_phase_count": (C.c_int, [C.c_int]),
     "q3l_phase_name": (C.c_char_p, [C.c_int, C.c_int]),
+    "q3l_model_validate": (C.c_int, [C.POINTER(ModelCfg)]),
+    "q3l_model_saved_bytes": (_sz, [C.POINTER(ModelCfg)]),
+    "q3l_model_workspace_bytes": (_sz, [C.POINTER(ModelCfg), C.c_int]),
+    "q3l_model_forward": (C.c_int, [C.POINTER(ModelCfg), C.POINTER(ModelWeights),
+                                    _vp, _vp, _vp, _vp, _sz, _vp, C.POINTER(Exec)]),
+    "q3l_model_backward": (C.c_int, [C.POINTER(ModelCfg), C.POINTER(ModelWeights),
+                                     _vp, _vp, _vp, C.POINTER(ModelGrads), C.c_int,
+                                     _vp, _sz, _vp]),
     "q3l_last_error": (C.c_char_p, []),
     "q3l_version": (C.c_int, []),
     "q3l_rmsnorm_fwd": (C.c_int, [_i32, _i64, _i32, _vp, _vp, _f, _vp, _vp,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq3layer.so")
-SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "norm.hip", "attn_state.hip",
+SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "norm.hip", "attn_state.hip", "embed.hip",
            "attn_bf16.hip", "attn_f32.hip", "transpose.hip", "swiglu.hip"]
 ARCH = "gfx950"
 # Per-source flags.  The attention kernels run softmax arithmetic on their

@@ -1253,3 +1253,300 @@ extern "C" q3l_status q3l_attention_bwd_noalloc(
   return q3l_attention_bwd(dtype, B, L, h_q, h_kv, d_h, q, ldq, k, ldk, v, ldv, o, ldo, dout,
                            lddo, lse, dq, dk, dv, ws, kScratchFloats * sizeof(float), stream);
 }
+
+// ---------------------------------------------------------------------------
+// The model around a stack of layers: embedding gather, the layers, the final
+// RMSNorm and the tied output projection, and the backward in reverse.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kModelMaxTokens = 262144;   // the embedding scatter's link scan
+
+struct ModelSaved {
+  size_t xs;        // (n_layers + 1) layer inputs / the last output, [T, d] each
+  size_t x_stride;  // bytes between them
+  size_t hf, rf;    // final norm output [T, d] and its rstd [T] fp32
+  size_t layers;    // n_layers layer saved blocks (no recompute)
+  size_t layer_stride;
+  size_t total;
+};
+
+ModelSaved model_saved_layout(const q3l_model_cfg& c) {
+  const Dims m = dims_of(c.layer);
+  ModelSaved s{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+  s.x_stride = up(m.T * m.d * m.es);
+  s.xs = take(s.x_stride * (size_t)(c.n_layers + 1));
+  s.hf = take(m.T * m.d * m.es);
+  s.rf = take(m.T * 4);
+  s.layer_stride = up(saved_layout(c.layer).total);
+  s.layers = take(c.recompute ? 0 : s.layer_stride * (size_t)c.n_layers);
+  s.total = off;
+  return s;
+}
+
+// Forward scratch: two x buffers and hf / rf (inference), and one layer's
+// forward workspace.
+struct ModelFwdWs { size_t xa, xb, hf, rf, layer, layer_bytes, total; };
+ModelFwdWs model_fwd_ws(const q3l_model_cfg& c) {
+  const Dims m = dims_of(c.layer);
+  ModelFwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+  w.xa = take(m.T * m.d * m.es);
+  w.xb = take(m.T * m.d * m.es);
+  w.hf = take(m.T * m.d * m.es);
+  w.rf = take(m.T * 4);
+  w.layer_bytes = saved_layout(c.layer).wt;
+  w.layer = take(w.layer_bytes);
+  w.total = off;
+  return w;
+}
+
+// Backward scratch: the layer backward's workspace, two dx buffers, dhf, the
+// final norm's partial sums, the embedding scatter's links, a layer's saved
+// block and output for recomputation, and (bf16) the transposed operands of
+// the output projection's two GEMMs.
+struct ModelBwdWs {
+  size_t layer, layer_bytes, dxa, dxb, dhf, wpart, next, first, rsaved, ry, et, dlt, hft, total;
+};
+ModelBwdWs model_bwd_ws(const q3l_model_cfg& c) {
+  const Dims m = dims_of(c.layer);
+  ModelBwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+  w.layer_bytes = bwd_layout(c.layer).total;
+  w.layer = take(w.layer_bytes);
+  w.dxa = take(m.T * m.d * m.es);
+  w.dxb = take(m.T * m.d * m.es);
+  w.dhf = take(m.T * m.d * m.es);
+  w.wpart = take((size_t)rmsnorm_bwd_max_parts() * m.d * 4);
+  w.next = take(m.T * 4);
+  w.first = take(m.T * 4);
+  w.rsaved = take(c.recompute ? saved_layout(c.layer).total : 0);
+  w.ry = take(c.recompute ? m.T * m.d * m.es : 0);
+  const size_t V = (size_t)c.vocab, Tp = (size_t)pad8(m.T);
+  const bool bt = c.layer.dtype == Q3L_BF16;
+  w.et = take(bt ? (size_t)m.d * V * 2 : 0);
+  w.dlt = take(bt ? V * Tp * 2 : 0);
+  w.hft = take(bt ? (size_t)m.d * Tp * 2 : 0);
+  w.total = off;
+  return w;
+}
+
+q3l_status model_validate(const q3l_model_cfg* c) {
+  if (!c) return fail(Q3L_EINVAL, "model cfg is NULL");
+  q3l_status st = validate(&c->layer);
+  if (st != Q3L_OK) return st;
+  if (c->layer.tp_partial) return fail(Q3L_EUNSUPPORTED, "a model stack has no tp_partial layers");
+  if (c->n_layers < 0) return fail(Q3L_EINVAL, "n_layers=%d is negative", c->n_layers);
+  if (c->vocab <= 0 || c->vocab % 8) return fail(Q3L_EINVAL, "vocab=%d must be a positive multiple of 8", c->vocab);
+  if (c->recompute != 0 && c->recompute != 1) return fail(Q3L_EINVAL, "recompute must be 0 or 1");
+  const int64_t T = (int64_t)c->layer.B * c->layer.L, V = c->vocab, d = c->layer.d;
+  if (T > kModelMaxTokens)
+    return fail(Q3L_EUNSUPPORTED, "B*L=%lld exceeds the %lld tokens of the embedding scatter",
+                (long long)T, (long long)kModelMaxTokens);
+  if (c->layer.dtype == Q3L_BF16 &&
+      ((T + 8) * V * 2 >= (1LL << 31) || (V + 8) * d * 2 >= (1LL << 31) ||
+       (V + 8) * pad8(T) * 2 >= (1LL << 31)))
+    return fail(Q3L_EUNSUPPORTED, "logits [%lld, %lld] or the table exceed the 2 GiB offset "
+                "range of the bf16 GEMM", (long long)T, (long long)V);
+  return Q3L_OK;
+}
+
+q3l_status check_model_weights(const q3l_model_cfg& c, const q3l_model_weights* w) {
+  if (!w) return fail(Q3L_EINVAL, "model weights struct is NULL");
+  Q3L_CHECK_PTR(w->embed, "w.embed");
+  Q3L_CHECK_PTR(w->final_norm, "w.final_norm");
+  if (c.n_layers > 0 && !w->layers) return fail(Q3L_EINVAL, "w.layers is NULL");
+  for (int i = 0; i < c.n_layers; ++i) {
+    const q3l_status st = check_weights(&w->layers[i], c.layer.qk_norm != 0);
+    if (st != Q3L_OK) {
+      const std::string msg = g_err;
+      return fail(st, "layer %d: %s", i, msg.c_str());
+    }
+  }
+  return Q3L_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q3l_status q3l_model_validate(const q3l_model_cfg* cfg) {
+  const q3l_status st = model_validate(cfg);
+  if (st == Q3L_OK) g_err.clear();
+  return st;
+}
+
+size_t q3l_model_saved_bytes(const q3l_model_cfg* cfg) {
+  if (model_validate(cfg) != Q3L_OK) return 0;
+  return model_saved_layout(*cfg).total;
+}
+
+size_t q3l_model_workspace_bytes(const q3l_model_cfg* cfg, int backward) {
+  if (model_validate(cfg) != Q3L_OK) return 0;
+  return backward ? model_bwd_ws(*cfg).total : model_fwd_ws(*cfg).total;
+}
+
+q3l_status q3l_model_forward(const q3l_model_cfg* cfg, const q3l_model_weights* w,
+                             const int32_t* ids, void* logits, void* saved, void* workspace,
+                             size_t workspace_bytes, void* stream, const q3l_exec* exec) {
+  q3l_status st = model_validate(cfg);
+  if (st != Q3L_OK) return st;
+  const q3l_model_cfg& c = *cfg;
+  if ((st = check_model_weights(c, w)) != Q3L_OK) return st;
+  Q3L_CHECK_PTR(ids, "ids");
+  Q3L_CHECK_PTR(logits, "logits");
+  Q3L_CHECK_PTR(workspace, "workspace");
+  if (saved) Q3L_CHECK_PTR(saved, "saved");
+  if (exec && (exec->marks || exec->n_marks))
+    return fail(Q3L_EINVAL, "exec.marks are per layer call; pass none to the model calls");
+  if (exec && exec->side_stream && (!exec->fork_event || !exec->join_event))
+    return fail(Q3L_EINVAL, "exec.side_stream needs exec.fork_event and exec.join_event");
+  const ModelFwdWs FW = model_fwd_ws(c);
+  if (workspace_bytes < FW.total)
+    return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, FW.total);
+  const ModelSaved MS = model_saved_layout(c);
+  const Dims m = dims_of(c.layer);
+  const int dt = c.layer.dtype;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Layer inputs: in `saved` for a training forward, else two alternating
+  // scratch buffers.
+  auto xbuf = [&](int i) -> char* {
+    if (saved) return at(saved, MS.xs + MS.x_stride * (size_t)i);
+    return at(workspace, (i & 1) ? FW.xb : FW.xa);
+  };
+  char* hf = saved ? at(saved, MS.hf) : at(workspace, FW.hf);
+  float* rf = reinterpret_cast<float*>(saved ? at(saved, MS.rf) : at(workspace, FW.rf));
+  Q3L_HIP(embed_gather(dt, m.T, m.d, c.vocab, ids, w->embed, xbuf(0), s));
+  for (int i = 0; i < c.n_layers; ++i) {
+    q3l_outputs out{};
+    out.y = xbuf(i + 1);
+    void* ls = (saved && !c.recompute) ? at(saved, MS.layers + MS.layer_stride * (size_t)i)
+                                       : nullptr;
+    st = q3l_layer_forward(&c.layer, &w->layers[i], xbuf(i), &out, ls,
+                           at(workspace, FW.layer), FW.layer_bytes, stream, exec);
+    if (st != Q3L_OK) return st;
+  }
+  Q3L_HIP(rmsnorm_fwd(dt, m.T, m.d, xbuf(c.n_layers), w->final_norm, c.layer.eps, hf, rf, s));
+  // Output projection, tied to the embedding table: logits = hf E^T.
+  GemmArgs g{};
+  g.a = kop(hf, m.d, (int)m.T);
+  g.b = kop(w->embed, m.d, c.vocab);
+  g.M = (int)m.T; g.N = c.vocab; g.K = m.d;
+  g.epi = epi_store(logits, c.vocab, nullptr, 0);
+  Q3L_HIP(gemm(dt, g, s));
+  g_err.clear();
+  return Q3L_OK;
+}
+
+q3l_status q3l_model_backward(const q3l_model_cfg* cfg, const q3l_model_weights* w,
+                              const int32_t* ids, const void* dlogits, const void* saved,
+                              const q3l_model_grads* grads, int flags, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  q3l_status st = model_validate(cfg);
+  if (st != Q3L_OK) return st;
+  const q3l_model_cfg& c = *cfg;
+  if ((st = check_model_weights(c, w)) != Q3L_OK) return st;
+  if (flags & ~Q3L_BWD_ACCUMULATE)
+    return fail(Q3L_EINVAL, "model backward flags: only Q3L_BWD_ACCUMULATE (0x%x given)", flags);
+  const int acc = (flags & Q3L_BWD_ACCUMULATE) ? 1 : 0;
+  Q3L_CHECK_PTR(ids, "ids");
+  Q3L_CHECK_PTR(dlogits, "dlogits");
+  Q3L_CHECK_PTR(saved, "saved");
+  Q3L_CHECK_PTR(workspace, "workspace");
+  if (!grads) return fail(Q3L_EINVAL, "grads struct is NULL");
+  Q3L_CHECK_PTR(grads->embed, "grads.embed");
+  Q3L_CHECK_PTR(grads->final_norm, "grads.final_norm");
+  if (c.n_layers > 0 && !grads->layers) return fail(Q3L_EINVAL, "grads.layers is NULL");
+  const ModelBwdWs BW = model_bwd_ws(c);
+  if (workspace_bytes < BW.total)
+    return fail(Q3L_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, BW.total);
+  const ModelSaved MS = model_saved_layout(c);
+  const Dims m = dims_of(c.layer);
+  const int dt = c.layer.dtype;
+  const bool bt = dt == Q3L_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = (int)m.T, Tp = (int)pad8(m.T), V = c.vocab, d = m.d;
+  auto xin = [&](int i) { return at(saved, MS.xs + MS.x_stride * (size_t)i); };
+  const char* hf = at(saved, MS.hf);
+  const float* rf = reinterpret_cast<const float*>(at(saved, MS.rf));
+  char* dhf = at(workspace, BW.dhf);
+  // Output projection: dhf = dlogits E, dE (+)= dlogits^T hf.
+  {
+    GemmArgs g{};
+    g.a = kop(dlogits, V, T);
+    if (bt) {
+      char* et = at(workspace, BW.et);
+      const TransposeJob job{w->embed, d, et, V, V, V, d};
+      Q3L_HIP(transpose_bf16_batch(&job, 1, s));
+      g.b = kop(et, V, d);
+    } else {
+      g.b = rop(w->embed, d, d);
+    }
+    g.M = T; g.N = d; g.K = V;
+    g.epi = epi_store(dhf, d, nullptr, 0);
+    Q3L_HIP(gemm(dt, g, s));
+  }
+  {
+    GemmArgs g{};
+    if (bt) {
+      char* dlt = at(workspace, BW.dlt);
+      char* hft = at(workspace, BW.hft);
+      const TransposeJob jobs[2] = {{dlogits, V, dlt, Tp, T, Tp, V}, {hf, d, hft, Tp, T, Tp, d}};
+      Q3L_HIP(transpose_bf16_batch(jobs, 2, s));
+      g.a = kop(dlt, Tp, V);
+      g.b = kop(hft, Tp, d);
+      g.K = Tp;
+    } else {
+      g.a = rop(dlogits, V, V);
+      g.b = rop(hf, d, d);
+      g.K = T;
+    }
+    g.M = V; g.N = d;
+    g.epi = epi_wgrad(grads->embed, d, acc);
+    Q3L_HIP(gemm(dt, g, s));
+  }
+  // Final RMSNorm.
+  char* dxs[2] = {at(workspace, BW.dxa), at(workspace, BW.dxb)};
+  {
+    float* wp = reinterpret_cast<float*>(at(workspace, BW.wpart));
+    int np = 0;
+    Q3L_HIP(rmsnorm_bwd(dt, m.T, d, dhf, xin(c.n_layers), rf, w->final_norm, nullptr, dxs[0],
+                        wp, &np, s));
+    Q3L_HIP(reduce_rows(wp, np, d, grads->final_norm, acc, s));
+  }
+  // Layers, last first.
+  int cur = 0;
+  for (int i = c.n_layers - 1; i >= 0; --i) {
+    const void* ls;
+    if (c.recompute) {
+      q3l_outputs out{};
+      out.y = at(workspace, BW.ry);
+      void* rs = at(workspace, BW.rsaved);
+      st = q3l_layer_forward(&c.layer, &w->layers[i], xin(i), &out, rs, nullptr, 0, stream,
+                             nullptr);
+      if (st != Q3L_OK) return st;
+      ls = rs;
+    } else {
+      ls = at(saved, MS.layers + MS.layer_stride * (size_t)i);
+    }
+    st = q3l_layer_backward(&c.layer, &w->layers[i], xin(i), dxs[cur], ls, dxs[cur ^ 1],
+                            &grads->layers[i], Q3L_BWD_INPUT | Q3L_BWD_WEIGHT | flags,
+                            at(workspace, BW.layer), BW.layer_bytes, stream, nullptr);
+    if (st != Q3L_OK) return st;
+    cur ^= 1;
+  }
+  // Embedding: scatter-add dx_0 into the table's gradient (after the output
+  // projection's part, so the order of the two additions is fixed).
+  Q3L_HIP(embed_scatter_add(dt, T, d, V, ids, dxs[cur],
+                            reinterpret_cast<int32_t*>(at(workspace, BW.next)),
+                            reinterpret_cast<int32_t*>(at(workspace, BW.first)), grads->embed,
+                            s));
+  g_err.clear();
+  return Q3L_OK;
+}
+
+}  // extern "C"

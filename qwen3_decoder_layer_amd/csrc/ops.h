@@ -139,6 +139,16 @@ int qknorm_bwd_max_parts();
 // The partial-row count qknorm_rope_bwd reports (heads = h_q + h_kv).
 int qknorm_bwd_parts(int64_t tokens, int heads, int d_h);
 
+// ---- token embedding ------------------------------------------------------
+// x[t] = E[ids[t]] (zero rows for ids outside [0, V)); d a multiple of 8.
+hipError_t embed_gather(int dtype, int64_t T, int d, int V, const int32_t* ids, const void* E,
+                        void* x, hipStream_t s);
+// dE[v] += sum over t with ids[t] = v of dx[t] (fp32, fixed order); next and
+// first are [T] int32 scratch.  d <= 8192.
+hipError_t embed_scatter_add(int dtype, int T, int d, int V, const int32_t* ids,
+                             const void* dx, int32_t* next, int32_t* first, float* dE,
+                             hipStream_t s);
+
 // ---- attention ------------------------------------------------------------
 struct AttnArgs {
   int B, L, h_q, h_kv, d_h;

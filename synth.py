@@ -125,3 +125,23 @@ def preset_inputs(idx: int) -> tuple[dict, dict]:
     """The preset workload `idx` with its conventional seed 1000 + idx."""
     cfg = preset(idx)
     return cfg, make_inputs(cfg, 1000 + idx)
+
+
+def make_model_inputs(cfg: dict, n_layers: int, vocab: int, seed: int) -> dict:
+    """Inputs of a stack of n_layers layers with the model's ends: token ids
+    [B, L] (uniform in [0, vocab), with repeats), the embedding table
+    [vocab, d] ~ N(0, 1) (so embedded rows have the layer workload's x
+    distribution), the final norm weight 1 + N(0, 0.1), each layer's eleven
+    parameters (make_inputs with seeds seed + 1 + i, x and dy unused) and
+    dlogits [B, L, vocab] ~ N(0, 1).  Values rounded like make_inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = cfg["dtype"]
+    out = {"ids": rng.integers(0, vocab, size=(cfg["B"], cfg["L"]), dtype=np.int64).astype(np.int32)}
+    out["embed"] = _draw(rng, (vocab, cfg["d"]), 0.0, 1.0, dt)
+    out["final_norm"] = _draw(rng, (cfg["d"],), 1.0, 0.1, dt)
+    out["dlogits"] = _draw(rng, (cfg["B"], cfg["L"], vocab), 0.0, 1.0, dt)
+    out["layers"] = []
+    for i in range(n_layers):
+        li = make_inputs(cfg, seed + 1 + i)
+        out["layers"].append({n: li[n] for n in PARAM_NAMES})
+    return out
