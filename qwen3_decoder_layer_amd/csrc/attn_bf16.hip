@@ -190,12 +190,26 @@ struct TrOffsets {
 // ring-attention merge: m = the largest scaled score (natural log), l = sum
 // of exp(score - m), acc = sum of exp(score - m) v (fp32); rows with no
 // visible key get (-inf, 0, 0).
+//
+// Each K/V tile t is one iteration of two phases of pinned slots (one
+// matrix instruction each, scheduling barriers between slots), so a wave's
+// own softmax arithmetic runs while its matrix instructions execute:
+//   A: the 16 score products of tile t+1 (S^T = K Q^T), each slot carrying
+//      two exponentials and row-sum adds of tile t's probabilities and the
+//      K fragment read two slots ahead;
+//   B: the 16 products O^T += V^T P^T of tile t, each slot carrying the row
+//      maximum (and, at the diagonal or the sequence end, the mask) of two
+//      of tile t+1's scores and the V^T fragment read two slots ahead.
+// After B the running maximum is moved for tile t+1 (rarely: only when it
+// grows by more than kTau), rescaling O and l.
 template <int DH, bool STATE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   constexpr int NKK = DH / 16;   // k-steps over the head dim
   constexpr int NDT = DH / 32;   // 32-row tiles of d
   constexpr int RB = 2 * DH, CPR = RB / 16;
   constexpr int TB = KT * RB;    // one K or V tile
+  constexpr int NSA = 2 * NKK;   // A slots (score products)
+  constexpr int NSB = 4 * NDT;   // B slots (P V products)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TB];   // 2 K slots, 2 V slots
   Q3L_LDS char* lds = (Q3L_LDS char*)smem;
 
@@ -223,53 +237,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
   const int tb = STATE ? p.k_lo / KT : 0;
   const int ntiles = (kend_g + KT - 1) / KT - tb;
   const int my_tiles = qw0 < L ? (kend_w + KT - 1) / KT - tb : 0;
+  const int qrow = qw0 + l32;
 
   // Q fragments (second MFMA operand: lane owns query row qw0 + l32).
   u32x4_t qf[NKK];
   {
-    const int qr = min(qw0 + l32, L - 1);
+    const int qr = min(qrow, L - 1);
     const bf16_t* qp = p.q + (tok0 + qr) * p.ldq + (int64_t)head * DH + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = ld16(qp + 16 * kk);
   }
-
-  // K and V tiles by direct loads; V^T operands by transposing reads.  The
-  // loop is software-pipelined: iteration t computes the scores of tile
-  // t+1 while it finishes tile t (softmax, then P V), so the matrix cores
-  // have independent work during the exponentials.  K and V therefore have
-  // their own two slots each with shifted lifetimes: iteration t reads
-  // K(t+1) and V(t), and starts loading K(t+2) and V(t+1) into the slots
-  // that K(t) and V(t-1) left (both drained before the previous barrier).
-  auto kslot = [&](int s) { return lds + s * TB; };
-  auto vslot = [&](int s) { return lds + (2 + s) * TB; };
-  auto load_k = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.k, p.ldk, tok0, kvh * DH, (tb + t) * KT, L, kslot(s), wave,
-                             lane);
-  };
-  auto load_v = [&](int t, int s) {
-    load_rows_lds<DH, KT, 4>(p.v, p.ldv, tok0, kvh * DH, (tb + t) * KT, L, vslot(s), wave,
-                             lane);
-  };
-  uint32_t offk[NKK];
-  {
-    const int sw = swz<CPR>(l32);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) offk[kk] = (uint32_t)(((2 * kk + h) ^ sw) << 4);
-  }
-  const uint32_t rowk = (uint32_t)l32 * RB;
-  TrOffsets<DH> tro;
-  tro.init(lane);
-  // S^T of one tile (lane: one query, 2 x 16 keys).
-  auto scores = [&](const Q3L_LDS char* sK, f32x16_t (&sc)[2]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[c][e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        sc[c] = mfma32(ld_lds16(sK + rowk + 32u * RB * c + offk[kk]), qf[kk], sc[c]);
-    }
-  };
 
   f32x16_t oacc[NDT];
 #pragma unroll
@@ -278,7 +255,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   float m_max = -INFINITY;   // block form: the exact row maximum (log2 units)
-  const int qrow = qw0 + l32;
 
   if constexpr (STATE) {
     // No key of the range is visible to any row of the workgroup (uniform).
@@ -300,94 +276,225 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
     }
   }
 
+  // K and V tiles by direct loads from one per-lane offset fixed across
+  // tiles (a scalar buffer resource per tile, ending at the sequence end).
+  // Iteration t reads K(t+1) and V(t) and starts loading K(t+2) and V(t+1)
+  // into the slots K(t) and V(t-1) left.
+  auto kslot = [&](int s) { return lds + s * TB; };
+  auto vslot = [&](int s) { return lds + (2 + s) * TB; };
+  TileLoader<DH, KT, 4> kld, vld;
+  kld.init(p.ldk, wave, lane);
+  vld.init(p.ldv, wave, lane);
+  auto load_k = [&](int t, int s) {
+    kld.load(p.k, p.ldk, tok0, kvh * DH, (tb + t) * KT, L, kslot(s), wave);
+  };
+  auto load_v = [&](int t, int s) {
+    vld.load(p.v, p.ldv, tok0, kvh * DH, (tb + t) * KT, L, vslot(s), wave);
+  };
+  // K fragment of k-step kk, key block c: row 32 c + l32, chunk 2 kk + h
+  // at slot (2 kk + h) ^ swz(l32) = 2 kk ^ (h ^ swz): a per-lane base XOR
+  // 32 kk, plus the block and slot offsets (multiples of 1 KiB).  The
+  // NKK XORed bases are computed once, so each fragment read is one LDS
+  // instruction with the block and slot offsets as immediates.
+  const uint32_t kbase =
+      lds_addr(lds) + (uint32_t)l32 * RB + ((uint32_t)(h ^ swz<CPR>(l32)) << 4);
+  uint32_t kx[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kx[kk] = kbase ^ (32u * kk);
+  // V^T operand reads: the two transposing reads of d block dt come from
+  // per-lane bases cx[i] ^ 64 dt (TrOffsets::read_x), also computed once.
+  TrOffsets<DH> tro;
+  tro.init(lane);
+  uint32_t vx[2][NDT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vx[i][dt] = (lds_addr(lds) + tro.cx[i]) ^ (64u * dt);
+
+  f32x16_t sc[2][2];          // scores of tiles t (slot t % 2) and t+1
+  // Mask of tile kv0: element (c, e) holds key kv0 + 4h + off(c, e) with
+  // off = 32 c + 8 (e / 4) + e % 4 (a constant), visible iff off <= hi and
+  // off >= lo -- two per-lane limits per tile, one compare per element.
+  struct Lim { int lo, hi; };
+  auto limits = [&](int kv0) __attribute__((always_inline)) {
+    const int base = kv0 + 4 * h;
+    int hi = min(qrow, L - 1) - base;
+    int lo = 0;
+    if constexpr (STATE) {
+      hi = min(hi, p.k_hi - 1 - base);
+      lo = p.k_lo - base;
+    }
+    return Lim{lo, hi};
+  };
+  auto visible = [&](const Lim& lm, int c, int e) __attribute__((always_inline)) {
+    const int off = 32 * c + 8 * (e >> 2) + (e & 3);
+    if constexpr (STATE) return off <= lm.hi && off >= lm.lo;
+    return off <= lm.hi;
+  };
+  auto edge_tile = [&](int kv0) __attribute__((always_inline)) {
+    bool e = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
+    if constexpr (STATE) e = e || kv0 < p.k_lo || kv0 + KT > p.k_hi;
+    return e;
+  };
+  // Exchange of the two key halves' row maxima (a VALU lane swap between
+  // the half-waves), scaled to log2 units; then the reference maximum moves
+  // (and O, l are rescaled) only when a row's maximum exceeds it by more
+  // than kTau: exponents stay <= kTau, the result is exact, and the
+  // 64-multiply rescale is usually skipped.
+  auto settle_max = [&](float mx) __attribute__((always_inline)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                    false, false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.scale_log2;
+    if constexpr (STATE) m_max = fmaxf(m_max, mx);
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      // (Block form: a row with no visible key so far, beside rows that
+      // rescale, has m_run = m_new = -inf; its O and l are still zero.)
+      const float alpha = (STATE && m_new == -INFINITY) ? 0.f : exp2_raw(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    }
+  };
+
   load_k(0, 0);
   if (ntiles > 1) load_k(1, 1);
   load_v(0, 0);
   wait_vmcnt<0>();
   stage_barrier();
-  f32x16_t sc[2][2];          // scores of tiles t (slot t % 2) and t+1
-  scores(kslot(0), sc[0]);
+  // Prologue: scores of tile 0 and their row maximum.
+  {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[0][c][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sc[0][c] = mfma32(ld_lds16((const Q3L_LDS void*)(uintptr_t)(kx[kk] + 32u * RB * c)),
+                          qf[kk], sc[0][c]);
+    }
+    if (my_tiles > 0) {
+      const int kv0 = tb * KT;
+      float mx = -INFINITY;
+      if (edge_tile(kv0)) {
+        const Lim lm = limits(kv0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sc[0][c][e] = visible(lm, c, e) ? sc[0][c][e] : -INFINITY;
+            mx = fmaxf(mx, sc[0][c][e]);
+          }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[0][c][e]);
+      }
+      settle_max(mx);
+    }
+  }
   stage_barrier();            // K(0) read by every wave before its slot is refilled
+
   // Iteration t; the slot parity is a compile-time constant (two iterations
-  // per trip), so LDS addresses are a per-lane register plus an immediate.
-  auto iter = [&](int t, auto par) {
+  // per trip), so LDS slot offsets are immediates.
+  auto iter = [&](int t, auto par) __attribute__((always_inline)) {
     constexpr int s = decltype(par)::value;
     if (t + 2 < ntiles) load_k(t + 2, s);
     if (t + 1 < ntiles) load_v(t + 1, s ^ 1);
     if (t < my_tiles) {
       f32x16_t (&cur)[2] = sc[s];
-      const int kv0 = (tb + t) * KT;
-      // Row maximum; only tiles that reach the diagonal or the sequence end
-      // mask.  The two cases are separate straight-line code paths.
-      float mx = -INFINITY;
-      auto row_max = [&](auto masked) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float v = cur[c][e];
-            if constexpr (decltype(masked)::value) {
-              const int kv = kv0 + 32 * c + 8 * (e >> 2) + 4 * h + (e & 3);
-              bool out = kv > qrow || kv >= L;
-              if constexpr (STATE) out = out || kv < p.k_lo || kv >= p.k_hi;
-              v = out ? -INFINITY : v;
-              cur[c][e] = v;
-            }
-            mx = fmaxf(mx, v);
-          }
-      };
-      bool edge = (kv0 + KT - 1 > qw0) || (kv0 + KT > L);
-      if constexpr (STATE) edge = edge || kv0 < p.k_lo || kv0 + KT > p.k_hi;
-      if (edge)
-        row_max(std::true_type{});
-      else
-        row_max(std::false_type{});
-      // The two half-waves hold the two key halves of a query: exchange their
-      // maxima with a lane swap between the halves (a VALU op, no LDS queue).
-      {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-        mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * p.scale_log2;   // log2 units
-      }
-      if constexpr (STATE) m_max = fmaxf(m_max, mx);
-      // The reference maximum m_run moves (and O, l are rescaled) only when a
-      // row's maximum exceeds it by more than kTau: exponents stay <= kTau,
-      // the result is exact, and the 64-multiply rescale is usually skipped.
-      if (__any(mx > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        // (Block form: a row with no visible key so far, beside rows that
-        // rescale, has m_run = m_new = -inf; its O and l are still zero.)
-        const float alpha = (STATE && m_new == -INFINITY) ? 0.f : exp2_raw(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-      }
-      // Scores of tile t+1 (unused past this wave's last tile: the slot then
-      // holds another tile or stale data, which is harmless to read).
-      scores(kslot(s ^ 1), sc[s ^ 1]);
+      f32x16_t (&nx)[2] = sc[s ^ 1];
       // (Block form: a row that has seen no visible key yet keeps m_run =
       // -inf; its masked scores then give exp2(-inf) = 0, not NaN.)
       const float neg = (STATE && m_run == -INFINITY) ? 0.f : -m_run;
       float rs = 0.f;
+      u32x4_t pf[4];
+      // ---- A: scores of tile t+1, exponentials of tile t ----
+      {
+        auto kfrag = [&](int j) __attribute__((always_inline)) {
+          return ld_lds16((const Q3L_LDS void*)(uintptr_t)(
+              kx[j >> 1] + (uint32_t)((s ^ 1) * TB) + 32u * RB * (j & 1)));
+        };
+        u32x4_t ring[3];
+        ring[0] = kfrag(0);
+        ring[1] = kfrag(1);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int j = 0; j < NSA; ++j) {
+          const int c = j & 1, kk = j >> 1;
+          if (kk == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = exp2_raw(fmaf(cur[c][e], p.scale_log2, neg));
-          cur[c][e] = pv;
-          rs += pv;
+            for (int e = 0; e < 16; ++e) nx[c][e] = 0.f;
+          }
+          nx[c] = mfma32(ring[j % 3], qf[kk], nx[c]);
+          if (j + 2 < NSA) ring[(j + 2) % 3] = kfrag(j + 2);
+          constexpr int EPS = 32 / NSA;   // exponentials per slot
+#pragma unroll
+          for (int x = 0; x < EPS; ++x) {
+            const int q = EPS * j + x, cc = q >> 4, e = q & 15;
+            const float pv = exp2_raw(fmaf(cur[cc][e], p.scale_log2, neg));
+            cur[cc][e] = pv;
+            rs += pv;
+            // Each group of 8 probabilities goes to bf16 (an MFMA operand
+            // of phase B) as soon as it is complete.
+            if ((q & 7) == 7) pf[q >> 3] = pack_half(cur[cc], (q >> 3) & 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      l_run += rs;   // this half-wave's keys; the halves are added at the end
-      const Q3L_LDS char* sV = vslot(s);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t pf = pack_half(cur[ks >> 1], ks & 1);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(tro.read(sV, ks, dt), pf, oacc[dt]);
       }
+      l_run += rs;   // this half-wave's keys; the halves are added at the end
+      // ---- B: O^T += V^T P^T of tile t, row maximum of tile t+1 ----
+      const bool more = t + 1 < my_tiles;   // tile t+1 is this wave's too
+      const int kv1 = (tb + t + 1) * KT;
+      float mx = -INFINITY;
+      // Tiles that reach the diagonal or the sequence end (one or two per
+      // row) redo the maximum with the mask in a pass of their own after the
+      // slots: a second, masked copy of the pinned slots costs more
+      // registers than a wave has.
+      auto phase_b = [&](auto with_max) __attribute__((always_inline)) {
+        constexpr bool MAX = decltype(with_max)::value;
+        auto vfrag = [&](int j) __attribute__((always_inline)) {
+          const uint32_t o = (uint32_t)((2 + s) * TB) + 16u * RB * (uint32_t)(j / NDT);
+          const int dt = j % NDT;
+          const u32x2_t a = ld_tr8((const Q3L_LDS void*)(uintptr_t)(vx[0][dt] + o));
+          const u32x2_t b2 = ld_tr8((const Q3L_LDS void*)(uintptr_t)(vx[1][dt] + o));
+          return u32x4_t{a[0], a[1], b2[0], b2[1]};
+        };
+        u32x4_t ring[3];
+        ring[0] = vfrag(0);
+        ring[1] = vfrag(1);
+#pragma unroll
+        for (int j = 0; j < NSB; ++j) {
+          const int ks = j / NDT, dt = j % NDT;
+          oacc[dt] = mfma32(ring[j % 3], pf[ks], oacc[dt]);
+          if (j + 2 < NSB) ring[(j + 2) % 3] = vfrag(j + 2);
+          if constexpr (MAX) {
+            constexpr int MPS = 32 / NSB;   // maxima per slot
+#pragma unroll
+            for (int x = 0; x < MPS; ++x) {
+              const int q = MPS * j + x;
+              mx = fmaxf(mx, nx[q >> 4][q & 15]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      phase_b(std::true_type{});
+      if (more && edge_tile(kv1)) {
+        mx = -INFINITY;
+        const Lim lm = limits(kv1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            nx[c][e] = visible(lm, c, e) ? nx[c][e] : -INFINITY;
+            mx = fmaxf(mx, nx[c][e]);
+          }
+      }
+      if (more) settle_max(mx);
     }
     wait_vmcnt<0>();
     stage_barrier();
