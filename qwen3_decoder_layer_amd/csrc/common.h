@@ -120,23 +120,30 @@ constexpr uint32_t kOOB = 0x80000000u;   // any offset past the buffer range
 // uniform) is a byte offset and an offset >= 2^31 (kOOB) reads zeros.  These
 // writes are counted by vmcnt; a kernel orders them against its own LDS
 // reads with an explicit s_waitcnt vmcnt and a barrier.
-__device__ inline void lds_dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16,
-                                           voff, soff, 0, 0);
-}
-// The same through a given buffer resource, at per-lane voff + uniform soff.
+//
+// The instruction is written in inline assembly (M0 = LDS base, one wait
+// state, then buffer_load ... lds).  Issued through the compiler's builtin,
+// it makes the compiler put an s_waitcnt vmcnt(0) in front of every later
+// transposing LDS read (ds_read_b64_tr_b16), whatever address that reads:
+// each loop iteration would then wait, mid-iteration, for the prefetch it
+// has just issued.  The assembly form has no register results, so nothing
+// is left in flight towards a register the compiler could reuse, and the
+// compiler's own vmcnt counts (for its register loads) only over-wait, as
+// loads complete in issue order.
 __device__ inline void lds_dma16_r(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                    uint32_t lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 16, voff,
-                                           soff, 0, 0);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(soff), "s"(lds_base) : "memory", "m0");
+}
+__device__ inline void lds_dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  lds_dma16_r(__builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000),
+              voff, soff, lds_base);
 }
 __device__ inline void lds_dma4(uint64_t p, uint32_t voff, uint32_t lds_base) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q3L_LDS void*)(uintptr_t)lds_base, 4,
-                                           voff, 0, 0, 0);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds_base) : "memory", "m0");
 }
 
 // Buffer resource over [p, p + bytes) (bytes 0: every access is out of

@@ -458,18 +458,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     // contiguous bytes of bf16) instead of 16 bytes in each of 32 rows.  A
     // wave's LDS accesses execute in order, so a pass may overwrite the
     // region right after the previous pass's reads.
-    static_assert(WN == 64 && TM % EPASS == 0, "epilogue staging shape");
+    static_assert((WN == 64 || WN == 128) && TM % EPASS == 0, "epilogue staging shape");
     constexpr int BPP = TM / EPASS;            // 32-row blocks per pass
     constexpr int PR = 32 * BPP;               // rows per pass
-    constexpr int NT = PR / 4;                 // row groups per pass (plain epilogues)
+    constexpr int LPR = WN / 4;                // lanes per staged row (4 floats each)
+    constexpr int RPT = 64 / LPR;              // staged rows per read
+    constexpr int NT = PR / RPT;               // reads per pass (plain epilogues)
     Q3L_LDS char* reg = lds + wave * EREG;
     const int mw = m0 + wm * WM, nw = n0 + wn * WN;
-    // Plain epilogues: in pass p, lane reads staged row 4t + lane/16 (t <
-    // NT), columns 4 (lane % 16) .. +3.  The bf16 residual they add is
+    // Plain epilogues: in pass p, lane reads staged row RPT t + lane / LPR
+    // (t < NT), columns 4 (lane % LPR) .. +3.  The bf16 residual they add is
     // requested for every pass before the first barrier, at addresses
     // clamped into the matrix where the tile overhangs it, so the loads
     // overlap one another and the staging instead of each waiting in turn.
-    const int cn = 4 * (lane & 15), nn = nw + cn;
+    const int cn = 4 * (lane % LPR), nn = nw + cn;
     const int nclamp = nn < g.N ? nn : g.N - 4;
     const bf16_t* resid = nullptr;
     if constexpr (EPI == EPI_STORE) resid = static_cast<const bf16_t*>(e.r);
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
         for (int pass = 0; pass < EPASS; ++pass)
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            int m = mw + pass * PR + 4 * t + (lane >> 4);
+            int m = mw + pass * PR + RPT * t + lane / LPR;
             if (m > g.M - 1) m = g.M - 1;
             rr[pass][t] = ld8(resid + (int64_t)m * e.ldr + nclamp);
           }
@@ -510,15 +512,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
                 f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
           }
       if constexpr (EPI == EPI_SILU_MUL) {
-        // Staged row: g in columns 0..31, u in 32..63 (the paired operand
-        // interleaves 32-column blocks); f column = nw / 2 + c.
+        // Staged row: per 64-column block bb, g in columns 64 bb + 0..31
+        // and u in 64 bb + 32..63 (the paired operand interleaves 32-column
+        // blocks); f column = nw / 2 + 32 bb + c.
 #pragma unroll
-        for (int t = 0; t < PR / 8; ++t) {
-          const int row = 8 * t + (lane >> 3), c = 4 * (lane & 7);
-          const f32x4_t gv = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * c);
+        for (int t = 0; t < PR * (WN / 64) / 8; ++t) {
+          const int bb = t % (WN / 64), row = 8 * (t / (WN / 64)) + (lane >> 3);
+          const int c = 4 * (lane & 7);
+          const f32x4_t gv =
+              *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 256 * bb + 4 * c);
           const f32x4_t uv =
-              *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 128 + 4 * c);
-          const int m = mp + row, f = nw / 2 + c;
+              *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 256 * bb + 128 + 4 * c);
+          const int m = mp + row, f = nw / 2 + 32 * bb + c;
           if (m >= g.M || f >= e.ffn) continue;
           float fv[4];
 #pragma unroll
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
       } else {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int row = 4 * t + (lane >> 4);
+          const int row = RPT * t + lane / LPR;
           f32x4_t v = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * cn);
           const int m = mp + row;
           if (m >= g.M || nn >= g.N) continue;

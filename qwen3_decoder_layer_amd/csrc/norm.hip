@@ -373,14 +373,53 @@ __global__ void rope_table_kernel(int L, int d_h, double theta,
   const int t = idx / half, i = idx % half;
   const double inv = pow(theta, -2.0 * (double)i / (double)d_h);
   const double a = (double)t * inv;
-  cos_t[idx] = (float)cos(a);
-  sin_t[idx] = (float)sin(a);
+  // Reduced to [-pi, pi] first (Cody-Waite: 2 pi = C1 + C2 + C3, C1 and C2
+  // with 30 significant bits, so k C1 and k C2 are exact for k < 2^22):
+  // angles up to L radians would otherwise take the slow large-argument path
+  // of the fp64 cos / sin; the reduced angle is exact to about 1e-16 a.
+  const double C1 = 0x1.921fb54000000p+2, C2 = 0x1.10b4611800000p-28,
+               C3 = 0x1.313198a2e0370p-59;
+  const double k = rint(a * 0x1.45f306dc9c883p-3);   // a / (2 pi)
+  const double r = ((a - k * C1) - k * C2) - k * C3;
+  double sr, cr;
+  sincos(r, &sr, &cr);
+  cos_t[idx] = (float)cr;
+  sin_t[idx] = (float)sr;
 }
 
+// Eight elements of T as the raw words of their load (bf16: four, fp32:
+// eight), so a load in flight holds only its packed words.
+template <class T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4_t w;
+  __device__ void load(const bf16_t* p) { w = ld16(p); }
+  __device__ void get(float f[8]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[2 * j] = lo_f(w[j]); f[2 * j + 1] = hi_f(w[j]); }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ void get(float f[8]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[j] = a[j]; f[4 + j] = b[j]; }
+  }
+};
+
 // ---- q/k norm + RoPE forward ----------------------------------------------
-// One group of LP = d_h/8 lanes per (token, head) vector; lane j holds
-// elements 8j..8j+7.  Rotate-half pairing: element i (< d_h/2) pairs with
-// i + d_h/2, which sits in lane j ^ (LP/2).
+// One wave per token.  A (token, head) vector is held by a group of LP =
+// d_h/8 lanes, lane j of the group holding elements 8j..8j+7; the wave's
+// 64/LP groups take HPW consecutive heads per step.  Rotate-half pairing:
+// element i (< d_h/2) pairs with i + d_h/2, which sits in lane j ^ (LP/2).
+// The rotation row of the token's position and the two norm weights are the
+// same for every head of the token, so they are loaded once; the head
+// vectors of NB steps at a time are requested together, before the first of
+// them is used (NB = 5: 20 heads of 128 per request batch, the measured best
+// against 10, all 40 heads of the 8B shape).
 template <class T, int DH>
 __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
     int64_t tokens, int L, int h_q, int h_kv, int qk_norm, float eps,
@@ -388,53 +427,73 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(
     const T* __restrict__ wk, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, T* __restrict__ out, int64_t ld_out,
     float* __restrict__ rstd_q, float* __restrict__ rstd_k) {
-  constexpr int LP = DH / 8, HALF = LP / 2;
+  constexpr int LP = DH / 8, HALF = LP / 2, HPW = 64 / LP, NB = 5;
   const int lane = threadIdx.x & 63;
-  const int j = lane % LP;
+  const int j = lane % LP, grp = lane / LP;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= tokens) return;
   const int heads = h_q + h_kv;
-  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
-  const bool valid = item < tokens * heads;
-  const int64_t it = valid ? item : 0;
-  const int64_t t = it / heads;
-  const int hh = (int)(it % heads);
   const int pos = (int)(t % L);
-  const bool isq = hh < h_q;
-  // Every load (the vector, its norm weight, the rotation row) is issued
-  // before the first use: none waits behind the norm's reduction.
-  float v[8], wv[8], cs[8], sn[8];
-  V8<T>::load(in + t * ld_in + (int64_t)hh * DH + 8 * j, v);
-  if (qk_norm) V8<T>::load((isq ? wq : wk) + 8 * j, wv);
   const int i0 = 8 * (j % HALF);
-  V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
-  V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
-  float r = 1.f;
-  if (qk_norm) {
-    float ss = 0.f;
+  const T* src = in + t * ld_in + 8 * j;
+  T* dst = out + t * ld_out + 8 * j;
+  for (int h0 = 0; h0 < heads; h0 += NB * HPW) {
+    Raw8<T> raw[NB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-    ss = group_sum(ss, LP);
-    r = 1.0f / sqrtf(ss / (float)DH + eps);
+    for (int b = 0; b < NB; ++b) {
+      if (h0 + b * HPW >= heads) break;       // whole steps past the last head
+      // Groups past the last head (final step only) read the last head again.
+      raw[b].load(src + (int64_t)min(h0 + b * HPW + grp, heads - 1) * DH);
+    }
+    float cs[8], sn[8], wqv[8], wkv[8];
+    V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
+    V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
+    if (qk_norm) {
+      V8<T>::load(wq + 8 * j, wqv);
+      V8<T>::load(wk + 8 * j, wkv);
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * r * wv[e];
-  }
-  float pv[8];
+    for (int b = 0; b < NB; ++b) {
+      if (h0 + b * HPW >= heads) break;
+      const int hh = h0 + b * HPW + grp;
+      const bool isq = hh < h_q;
+      float v[8];
+      raw[b].get(v);
+      float r = 1.f;
+      if (qk_norm) {
+        float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pv[e] = __shfl_xor(v[e], HALF, 64);
-  float o[8];
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        ss = group_sum(ss, LP);
+        r = 1.0f / sqrtf(ss / (float)DH + eps);
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    o[e] = (j < HALF) ? v[e] * cs[e] - pv[e] * sn[e] : v[e] * cs[e] + pv[e] * sn[e];
-  if (!valid) return;
-  V8<T>::store(out + t * ld_out + (int64_t)hh * DH + 8 * j, o);
-  if (qk_norm && j == 0) {
-    if (isq) rstd_q[t * h_q + hh] = r;
-    else rstd_k[t * h_kv + (hh - h_q)] = r;
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * r * (isq ? wqv[e] : wkv[e]);
+      }
+      float pv[8], o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = __shfl_xor(v[e], HALF, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = (j < HALF) ? v[e] * cs[e] - pv[e] * sn[e] : v[e] * cs[e] + pv[e] * sn[e];
+      if (hh < heads) {
+        V8<T>::store(dst + (int64_t)hh * DH, o);
+        if (qk_norm && j == 0) {
+          if (isq) rstd_q[t * h_q + hh] = r;
+          else rstd_k[t * h_kv + (hh - h_q)] = r;
+        }
+      }
+    }
   }
 }
 
 // ---- q/k norm + RoPE backward ---------------------------------------------
 // g: gradient w.r.t. the rotated, normalised q/k.  Inverse rotation, then the
-// RMSNorm adjoint per head; dw_q / dw_k partial sums per block.
+// RMSNorm adjoint per head.  Lane roles and loads as in the forward; wave w
+// of the grid takes tokens w, w + (number of waves), ...  The
+// weight-gradient sums dn * x_hat stay in registers (every lane with the
+// same j holds the same eight weights), are added across the wave's lane
+// groups, then across its four waves through LDS in a fixed order: one
+// partial row of dw_q and of dw_k per workgroup.
 template <class T, int DH>
 __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
     int64_t tokens, int L, int h_q, int h_kv, int qk_norm,
@@ -444,71 +503,84 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
     const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     T* __restrict__ out, int64_t ld_out, float* __restrict__ wq_part,
     float* __restrict__ wk_part) {
-  constexpr int LP = DH / 8, HALF = LP / 2;
+  constexpr int LP = DH / 8, HALF = LP / 2, HPW = 64 / LP, NB = 3;
   __shared__ float sq[DH], sk[DH];
-  const int lane = threadIdx.x & 63;
-  const int j = lane % LP;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LP, grp = lane / LP;
   const int heads = h_q + h_kv;
   for (int i = threadIdx.x; i < DH; i += 256) { sq[i] = 0.f; sk[i] = 0.f; }
-  __syncthreads();
-  float aq[8], ak[8], wqv[8], wkv[8];
+  float aq[8], ak[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { aq[e] = 0.f; ak[e] = 0.f; }
-  if (qk_norm) {
-    V8<T>::load(wq + 8 * j, wqv);
-    V8<T>::load(wk + 8 * j, wkv);
-  }
-  const int64_t total = tokens * heads;
-  const int64_t stride = (int64_t)gridDim.x * (256 / LP);
-  const int64_t first = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LP;
-  const int64_t niter = (total + stride - 1) / stride;
-  for (int64_t k = 0; k < niter; ++k) {
-    const int64_t item = first + k * stride;
-    const bool valid = item < total;
-    const int64_t it = valid ? item : 0;
-    const int64_t t = it / heads;
-    const int hh = (int)(it % heads);
+  const int i0 = 8 * (j % HALF);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < tokens; t += nwaves) {
     const int pos = (int)(t % L);
-    const bool isq = hh < h_q;
-    // Every load of the item (gradient, rotation row, pre-norm vector and its
-    // rstd) is issued before the first use.
-    float gv[8], pg[8], cs[8], sn[8], xv[8];
-    V8<T>::load(g + t * ld_g + (int64_t)hh * DH + 8 * j, gv);
-    const int i0 = 8 * (j % HALF);
-    V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
-    V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
-    float r = 1.f;
-    if (qk_norm) {
-      V8<T>::load(pre + t * ld_pre + (int64_t)hh * DH + 8 * j, xv);
-      r = isq ? rstd_q[t * h_q + hh] : rstd_k[t * h_kv + (hh - h_q)];
-    }
+    const T* gsrc = g + t * ld_g + 8 * j;
+    const T* psrc = pre + t * ld_pre + 8 * j;
+    T* dst = out + t * ld_out + 8 * j;
+    for (int h0 = 0; h0 < heads; h0 += NB * HPW) {
+      // Every load of the token's steps (gradients, pre-norm vectors, their
+      // rstd, the rotation row, the norm weights) is issued before the
+      // first use.
+      Raw8<T> gr[NB], xr[NB];
+      float rr[NB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pg[e] = __shfl_xor(gv[e], HALF, 64);
-    float dn[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      dn[e] = (j < HALF) ? gv[e] * cs[e] + pg[e] * sn[e] : gv[e] * cs[e] - pg[e] * sn[e];
-    float o[8];
-    if (qk_norm) {
-      const float* wv = isq ? wqv : wkv;
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += dn[e] * wv[e] * xv[e] * r;
-      dot = group_sum(dot, LP) / (float)DH;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xh = xv[e] * r;
-        o[e] = r * (dn[e] * wv[e] - xh * dot);
-        if (valid) {
-          if (isq) aq[e] += dn[e] * xh;
-          else ak[e] += dn[e] * xh;
+      for (int b = 0; b < NB; ++b) {
+        if (h0 + b * HPW >= heads) break;
+        const int hh = min(h0 + b * HPW + grp, heads - 1);
+        gr[b].load(gsrc + (int64_t)hh * DH);
+        rr[b] = 1.f;
+        if (qk_norm) {
+          xr[b].load(psrc + (int64_t)hh * DH);
+          rr[b] = hh < h_q ? rstd_q[t * h_q + hh] : rstd_k[t * h_kv + (hh - h_q)];
         }
       }
-    } else {
+      float cs[8], sn[8], wqv[8], wkv[8];
+      V8<float>::load(cos_t + (int64_t)pos * (DH / 2) + i0, cs);
+      V8<float>::load(sin_t + (int64_t)pos * (DH / 2) + i0, sn);
+      if (qk_norm) {
+        V8<T>::load(wq + 8 * j, wqv);
+        V8<T>::load(wk + 8 * j, wkv);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = dn[e];
+      for (int b = 0; b < NB; ++b) {
+        if (h0 + b * HPW >= heads) break;
+        const int hh = h0 + b * HPW + grp;
+        const bool isq = hh < h_q, ok = hh < heads;
+        const float r = rr[b];
+        float gv[8], pg[8], dn[8], o[8];
+        gr[b].get(gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pg[e] = __shfl_xor(gv[e], HALF, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          dn[e] = (j < HALF) ? gv[e] * cs[e] + pg[e] * sn[e] : gv[e] * cs[e] - pg[e] * sn[e];
+        if (qk_norm) {
+          float wv[8], xv[8];
+          xr[b].get(xv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wv[e] = isq ? wqv[e] : wkv[e];
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot += dn[e] * wv[e] * xv[e] * r;
+          dot = group_sum(dot, LP) / (float)DH;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xh = xv[e] * r;
+            o[e] = r * (dn[e] * wv[e] - xh * dot);
+            if (ok) {
+              if (isq) aq[e] += dn[e] * xh;
+              else ak[e] += dn[e] * xh;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = dn[e];
+        }
+        if (ok) V8<T>::store(dst + (int64_t)hh * DH, o);
+      }
     }
-    if (valid) V8<T>::store(out + t * ld_out + (int64_t)hh * DH + 8 * j, o);
   }
   if (!qk_norm) return;
   // Lanes with the same j hold partials of the same 8 weights.
@@ -519,7 +591,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
       ak[e] += __shfl_xor(ak[e], o2, 64);
     }
   }
-  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // sq, sk cleared
   for (int w = 0; w < 4; ++w) {   // fixed order across waves
     if (wave == w && lane < LP) {
 #pragma unroll
@@ -536,7 +608,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
   }
 }
 
-constexpr int kQkBwdParts = 1024;
+constexpr int kQkBwdParts = 2048;
 
 // Workgroups (= partial rows of the weight gradient) of the RMSNorm
 // backward: bf16 at least 8 rows per workgroup, so the loads of the next rows
@@ -589,11 +661,11 @@ hipError_t rmsnorm_bwd_t(int64_t rows, int n, const void* dy, const void* x,
   return hipGetLastError();
 }
 
-// Workgroups (= partial rows) of the q/k norm backward: many small ones, so
-// enough waves keep loads in flight.
+// Workgroups (= partial rows) of the q/k norm backward: four waves of one
+// token at a time; one token per wave up to kQkBwdParts workgroups.
 int64_t qknorm_bwd_grid(int64_t tokens, int heads, int d_h) {
-  const int per_block = 256 / (d_h / 8);
-  int64_t grid = cdiv(tokens * heads, (int64_t)per_block * 8);
+  (void)heads; (void)d_h;
+  int64_t grid = cdiv(tokens, 4);
   if (grid > kQkBwdParts) grid = kQkBwdParts;
   if (grid < 1) grid = 1;
   return grid;
@@ -675,8 +747,7 @@ hipError_t qknorm_rope_fwd(int dtype, int B, int L, int h_q, int h_kv,
                            int64_t ld_out, float* rstd_q, float* rstd_k,
                            hipStream_t s) {
   const int64_t tokens = (int64_t)B * L;
-  const int64_t threads = tokens * (h_q + h_kv) * (d_h / 8);
-  dim3 grid((unsigned)cdiv(threads, 256)), block(256);
+  dim3 grid((unsigned)cdiv(tokens, 4)), block(256);   // one wave per token
 #define Q3L_QF(T, D)                                                          \
   hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, D>), grid, block, 0, s,       \
                      tokens, L, h_q, h_kv, qk_norm, eps, (const T*)in, ld_in, \
