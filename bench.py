@@ -84,14 +84,13 @@ def phase_work(c: dict) -> tuple:
     nqkv, nqk, heads = qd + 2 * kvd, qd + kvd, c["h_q"] + c["h_kv"]
     pairs = c["B"] * L * (L + 1) // 2
     a = 2                                   # bf16 bytes
-    w_bytes = a * (d * nqkv + qd * d + 3 * d * f)
     norm_fwd = ("hbm", 2 * a * T * d + 4 * T + a * d)
     norm_bwd = ("hbm", 4 * a * T * d + 4 * T + a * d)
     fwd = {
         "F1 rmsnorm": norm_fwd,
         "F2 qkv gemm": ("mfma", 2 * T * d * nqkv),
         "F3-F4 qk-norm + rope": ("hbm", 2 * a * T * nqk + 4 * T * heads + 8 * L * dh),
-        "transposes for the backward": ("hbm", 2 * w_bytes + 2 * a * T * d),
+        "transposes for the backward": ("hbm", 2 * a * T * d),
         "F5 attention": ("mfma", 4 * c["h_q"] * dh * pairs),
         "F6 o gemm + residual": ("mfma", 2 * T * qd * d),
         "F7 rmsnorm": norm_fwd,
@@ -154,7 +153,7 @@ def gpu_run(cfg: dict, inp: dict, steps: int, warmup: int) -> dict:
         ws = torch.empty(q3.workspace_bytes(lc, True), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
-    # The training forward's transposed copies run on this second stream,
+    # The training forward's transposed copy (xn^T) runs on this second stream,
     # beside the attention step (default priority, like every stream here).
     side = q3.Exec(side_stream=torch.cuda.Stream()) if backward else None
     nf, nb = len(q3.phase_names(False)), len(q3.phase_names(True))

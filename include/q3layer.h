@@ -127,14 +127,11 @@ typedef struct {
   size_t gu;       /* [T, 2*d_ffn] dtype: gate in columns [0, d_ffn), up in
                       [d_ffn, 2*d_ffn)                                     */
   size_t f;        /* [T, d_ffn] dtype, silu(gate) * up                    */
-  size_t wt;       /* bf16 with tp_partial == 0 only (else empty): the
-                      projection weights transposed to [in, out] for the
-                      backward's input-gradient GEMMs: W_down^T [d_ffn, d],
-                      then [W_gate; W_up]^T [d, 2*d_ffn], W_o^T [q_d, d],
-                      [W_q; W_k; W_v]^T [d, q_d + 2*kv_d] (q_d = h_q*d_h,
-                      kv_d = h_kv*d_h), each 256-byte aligned              */
-  size_t xnt;      /* as wt (else empty): xn^T [d, T8] with T8 = T rounded
-                      up to a multiple of 8, columns >= T zero             */
+  size_t wt;       /* empty (wt == xnt): the backward's input-gradient
+                      GEMMs read the projection weights as they are       */
+  size_t xnt;      /* bf16 with tp_partial == 0 only (else empty): xn^T
+                      [d, T8] with T8 = T rounded up to a multiple of 8,
+                      columns >= T zero (the QKV weight gradient's operand) */
   size_t total;    /* bytes of the whole buffer                            */
 } q3l_saved_layout;
 
@@ -143,11 +140,11 @@ typedef struct {
  * object named here is created and owned by the caller. */
 typedef struct {
   /* Optional second stream for work that depends only on the call's inputs:
-   * the bf16 training forward's transposed copies (saved wt and xnt), which
-   * then run beside the attention step.  NULL: they run on `stream`.  When
+   * the bf16 training forward's transposed copy (saved xnt), which
+   * then runs beside the attention step.  NULL: it runs on `stream`.  When
    * set, fork_event and join_event must be hipEvent_t the caller created
    * (timing may be disabled).  The call records fork_event on `stream`,
-   * makes side_stream wait for it, enqueues the copies on side_stream,
+   * makes side_stream wait for it, enqueues the copy on side_stream,
    * records join_event there and makes `stream` wait for it: all work of the
    * call stays ordered on `stream` (and can be captured into a HIP graph).
    * Calls that share these objects must not be made concurrently. */

@@ -129,33 +129,14 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
   s.hn = take(m.T * m.d * m.es);
   s.gu = take(m.T * 2 * (size_t)m.ffn * m.es);
   s.f = take(m.T * (size_t)m.ffn * m.es);
-  // Transposed copies for the backward (bf16): the weights, then xn^T.
+  // The transposed copy for the backward (bf16): xn^T.  (wt, once the
+  // transposed weights, is empty: the input-gradient GEMMs read the weights
+  // with transposing LDS loads.)
   s.wt = off;
-  if (has_transposes(c)) {
-    take((size_t)m.ffn * m.d * 2);
-    take((size_t)m.d * 2 * m.ffn * 2);
-    take((size_t)m.qd * m.d * 2);
-    take((size_t)m.d * m.nqkv * 2);
-  }
   s.xnt = off;
   if (has_transposes(c)) take((size_t)m.d * ((m.T + 7) / 8 * 8) * 2);
   s.total = off;
   return s;
-}
-
-// Offsets of the four transposed weights inside the saved wt region.
-struct WtLayout { size_t down, gu, o, qkv; };
-WtLayout wt_layout(const q3l_layer_cfg& c) {
-  const size_t ffn = (size_t)c.d_ffn, d = (size_t)c.d;
-  const size_t qd = (size_t)c.h_q * c.d_h, nqkv = qd + 2 * (size_t)c.h_kv * c.d_h;
-  WtLayout w{};
-  size_t off = 0;
-  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
-  w.down = take(ffn * d * 2);
-  w.gu = take(d * 2 * ffn * 2);
-  w.o = take(qd * d * 2);
-  w.qkv = take(d * nqkv * 2);
-  return w;
 }
 
 struct BwdWs {
@@ -369,29 +350,15 @@ q3l_status q3l_saved_layout_of(const q3l_layer_cfg* cfg, q3l_saved_layout* out) 
   return Q3L_OK;
 }
 
-// The copies the bf16 backward reads in K-contiguous form, from inputs the
-// forward already has: the seven projection weights transposed to [in, out]
-// and xn^T [d, Tp], in one launch.
-hipError_t transposed_copies(const q3l_layer_cfg& c, const q3l_weights* w, const void* xn,
-                             char* wt, char* xnt, hipStream_t s) {
+// The copy the bf16 backward reads in K-contiguous form, from an input the
+// forward already has: xn^T [d, Tp] (the QKV weight gradient's second
+// operand), columns >= T zero.
+hipError_t transposed_copies(const q3l_layer_cfg& c, const void* xn, char* xnt, hipStream_t s) {
   const Dims m = dims_of(c);
-  const WtLayout o = wt_layout(c);
-  const int d = m.d, ffn = m.ffn, qd = m.qd, kvd = m.kvd;
+  const int d = m.d;
   const int T = (int)m.T, Tp = (int)((m.T + 7) / 8 * 8);
-  char* wt_down = wt + o.down;
-  char* wt_gu = wt + o.gu;
-  char* wt_o = wt + o.o;
-  char* wt_qkv = wt + o.qkv;
-  const TransposeJob jobs[8] = {
-      {w->down, ffn, wt_down, d, d, d, ffn},
-      {w->gate, d, wt_gu, 2 * (int64_t)ffn, ffn, ffn, d},
-      {w->up, d, wt_gu + (size_t)ffn * 2, 2 * (int64_t)ffn, ffn, ffn, d},
-      {w->o, qd, wt_o, d, d, d, qd},
-      {w->q, d, wt_qkv, m.nqkv, qd, qd, d},
-      {w->k, d, wt_qkv + (size_t)qd * 2, m.nqkv, kvd, kvd, d},
-      {w->v, d, wt_qkv + (size_t)(qd + kvd) * 2, m.nqkv, kvd, kvd, d},
-      {xn, d, xnt, Tp, T, Tp, d}};
-  return transpose_bf16_batch(jobs, 8, s);
+  const TransposeJob jobs[1] = {{xn, d, xnt, Tp, T, Tp, d}};
+  return transpose_bf16_batch(jobs, 1, s);
 }
 
 size_t q3l_saved_bytes(const q3l_layer_cfg* cfg) {
@@ -482,7 +449,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   Q3L_HIP(mk.end(2));
   // The backward's transposed copies: on the caller's stream here, or on the
   // caller's second stream beside the attention step.
-  if (copies && !side) Q3L_HIP(transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), s));
+  if (copies && !side) Q3L_HIP(transposed_copies(c, xn, at(S, L.xnt), s));
   Q3L_HIP(mk.end(3));
   // Step 5: causal GQA attention.
   {
@@ -497,7 +464,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
       hipEvent_t join = static_cast<hipEvent_t>(exec->join_event);
       Q3L_HIP(hipEventRecord(fork, s));
       Q3L_HIP(hipStreamWaitEvent(side, fork, 0));
-      const hipError_t e1 = transposed_copies(c, w, xn, at(S, L.wt), at(S, L.xnt), side);
+      const hipError_t e1 = transposed_copies(c, xn, at(S, L.xnt), side);
       const hipError_t e2 = hipEventRecord(join, side);
       const hipError_t e3 = attn_fwd(dt, a, s);
       // Joined whatever happened above, so nothing of this call is left
@@ -649,19 +616,15 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   const int np_norm = rmsnorm_bwd_parts(dt, m.T, m.d);
   const int np_qk = qknorm_bwd_parts(m.T, m.hq + m.hkv, m.dh);
 
-  // bf16: every backward GEMM runs in the matrix-core kernel's K-contiguous
-  // form.  The weights transposed to [in, out], and xn^T, come from the
-  // saved block (the forward wrote them); the other operands of the
-  // weight-gradient GEMMs are transposed to [features, T] (T padded to a
-  // multiple of 8 with zeros) into reused scratch buffers.
+  // bf16: the input-gradient GEMMs read the weights [out, in] as they are,
+  // with the matrix-core kernel's transposing LDS loads (as fast as a
+  // transposed copy for all but the down projection, and no copy to write).
+  // The weight-gradient GEMMs contract over the tokens and run in the
+  // K-contiguous form: xn^T comes from the saved block (the forward wrote
+  // it), their other operands are transposed to [features, T] (T padded to
+  // a multiple of 8 with zeros) into reused scratch buffers.
   const bool bt = dt == Q3L_BF16;
   const int Tp = (int)pad8(m.T);
-  const WtLayout WT = wt_layout(c);
-  const char* wtb = bt ? at(saved, L.wt) : nullptr;
-  const char* wt_down = bt ? wtb + WT.down : nullptr;
-  const char* wt_gu = bt ? wtb + WT.gu : nullptr;
-  const char* wt_o = bt ? wtb + WT.o : nullptr;
-  const char* wt_qkv = bt ? wtb + WT.qkv : nullptr;
   const char* xnt = bt ? at(saved, L.xnt) : nullptr;
   char* tA = bt ? at(workspace, W.tA) : nullptr;
   char* tB = bt ? at(workspace, W.tB) : nullptr;
@@ -707,7 +670,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (chain) {
     GemmArgs g{};
     g.a = kop(dy, m.d, T);
-    g.b = bt ? kop(wt_down, m.d, m.ffn) : rop(w->down, m.ffn, m.ffn);
+    g.b = rop(w->down, m.ffn, m.ffn);
     g.M = T; g.N = m.ffn; g.K = m.d;
     if (bt) {
       g.epi = epi_store(dgu, 2 * (int64_t)m.ffn, nullptr, 0);
@@ -735,12 +698,8 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (chain) {
     GemmArgs g{};
     g.a = kop(dgu, 2 * (int64_t)m.ffn, T);
-    if (bt) {
-      g.b = kop(wt_gu, 2 * (int64_t)m.ffn, m.d);
-    } else {
-      g.b = rop(w->gate, m.d, m.d);
-      add_seg(g.b, w->up, m.d, m.ffn);
-    }
+    g.b = rop(w->gate, m.d, m.d);
+    add_seg(g.b, w->up, m.d, m.ffn);
     g.M = T; g.N = m.d; g.K = 2 * m.ffn;
     g.epi = epi_store(dhn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
@@ -763,7 +722,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (chain) {
     GemmArgs g{};
     g.a = kop(dh, m.d, T);
-    g.b = bt ? kop(wt_o, m.d, m.qd) : rop(w->o, m.qd, m.qd);
+    g.b = rop(w->o, m.qd, m.qd);
     g.M = T; g.N = m.qd; g.K = m.d;
     g.epi = epi_store(dO, m.qd, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));
@@ -802,13 +761,9 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   if (chain) {
     GemmArgs g{};
     g.a = kop(dqkv, m.nqkv, T);
-    if (bt) {
-      g.b = kop(wt_qkv, m.nqkv, m.d);
-    } else {
-      g.b = rop(w->q, m.d, m.d);
-      add_seg(g.b, w->k, m.d, m.qd);
-      add_seg(g.b, w->v, m.d, m.qd + m.kvd);
-    }
+    g.b = rop(w->q, m.d, m.d);
+    add_seg(g.b, w->k, m.d, m.qd);
+    add_seg(g.b, w->v, m.d, m.qd + m.kvd);
     g.M = T; g.N = m.d; g.K = m.nqkv;
     g.epi = epi_store(dxn, m.d, nullptr, 0);
     Q3L_HIP(gemm(dt, g, s));

@@ -145,26 +145,44 @@ struct KOperand {
 // for the K-contiguous form on transposed copies, so the layer's backward
 // still transposes its operands once; this form serves the stand-alone
 // gradient entry points and the layer without transposed copies.
-template <int R, int KB, int NW, bool MS>
+// MS: 0 one segment; 1 several segments along K, each starting at a
+// multiple of KB and all of one row stride (a slab lies in one segment);
+// 2 several segments in general.
+template <int R, int KB, int NW, int MS>
 struct ROperand {
   static constexpr int CPR = R / 8;
   static constexpr int RPI = 64 / CPR;
   static constexpr int NI = KB / (NW * RPI);
   int col[NI];        // per lane: global column of its chunk (clamped)
   int krl[NI];        // per lane: k-row within the slab
-  // Single-segment operand (MS false, the common case): per-lane byte
-  // offsets from the slab's first k-row, computed once, and the same for the
-  // last slab with kOOB where the k-row is past K; each request then adds
-  // only the uniform slab base.  A multi-segment operand (MS: weights
-  // stacked along K, read without a transposed copy) picks its segment per
-  // request.
-  uint64_t base0;     // uniform: segment 0 base
-  int64_t ld0;        // uniform: segment 0 row stride (elements)
+  // MS 0 and 1: per-lane byte offsets from the slab's first k-row,
+  // computed once, and the same for the last slab with kOOB where the k-row
+  // is past K; each request then adds only the uniform slab base (for MS 1,
+  // of the segment holding the slab).  MS 2 (weights stacked along K at
+  // starts that are not multiples of KB, read without a transposed copy)
+  // picks the segment per request.
+  uint64_t base0;                 // uniform: segment 0 base
+  uint64_t vb1, vb2;              // uniform (MS 1): segment bases minus start * ld * 2
+  int st1, st2;                   // uniform (MS 1): segment starts (past K if absent)
+  int64_t ld0;                    // uniform: row stride (elements)
   uint32_t voff[NI], vtail[NI];
 
   __device__ void init(const Operand& o, int r0, int K, int wave, int lane) {
     base0 = uni64((uint64_t)o.p[0]);
     ld0 = (int64_t)uni64((uint64_t)o.ld[0]);
+    if constexpr (MS == 1) {
+      // Segment s holds k-rows [st_s, st_{s+1}): k-row k of it is at
+      // p_s + (k - st_s) ld 2 = vb_s + k ld 2 (modulo 2^64).
+      // (Fixed fields, selected after reading: indexing the argument's
+      // arrays with a runtime index would copy them to scratch memory.)
+      const int n = (int)uni((uint32_t)o.nseg);
+      const int s1 = (int)uni((uint32_t)o.start[1]), s2 = (int)uni((uint32_t)o.start[2]);
+      const uint64_t p1 = uni64((uint64_t)o.p[1]), p2 = uni64((uint64_t)o.p[2]);
+      st1 = n > 1 ? s1 : 0x7fffffff;
+      st2 = n > 2 ? s2 : 0x7fffffff;
+      vb1 = n > 1 ? p1 - (uint64_t)((int64_t)s1 * ld0 * 2) : base0;
+      vb2 = n > 2 ? p2 - (uint64_t)((int64_t)s2 * ld0 * 2) : base0;
+    }
     const int klast = (K - 1) / KB * KB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -182,8 +200,18 @@ struct ROperand {
   __device__ void issue_one(const Operand& o, int i, int k0, int K, bool last,
                             Q3L_LDS char* dst, int wave) const {
     const uint32_t lds = uni(lds_addr(dst + 1024 * (NW * i + wave)));
-    if constexpr (!MS) {
+    if constexpr (MS == 0) {
       lds_dma16(base0 + (uint64_t)((int64_t)k0 * ld0 * 2), last ? vtail[i] : voff[i], 0u, lds);
+      return;
+    }
+    if constexpr (MS == 1) {
+      // Segment base by masks: written as selects, the choice makes the
+      // compiler keep the loader object in scratch memory.
+      const uint64_t m1 = 0ull - (uint64_t)(k0 >= st1), m2 = 0ull - (uint64_t)(k0 >= st2);
+      const uint64_t vb = base0 + ((vb1 - base0) & m1) + ((vb2 - vb1) & m2);
+      // (readfirstlane: the value is uniform, the compiler cannot tell)
+      lds_dma16(uni64(vb + (uint64_t)((int64_t)k0 * ld0 * 2)), last ? vtail[i] : voff[i], 0u,
+                lds);
       return;
     }
     const int q = NW * i + wave;
@@ -262,12 +290,12 @@ struct RFrag {
   }
 };
 
-template <int ROWS, int TT, int KB, int NW, bool KC, bool MS> struct OpSel;
-template <int ROWS, int TT, int KB, int NW, bool MS> struct OpSel<ROWS, TT, KB, NW, true, MS> {
+template <int ROWS, int TT, int KB, int NW, bool KC, int MS> struct OpSel;
+template <int ROWS, int TT, int KB, int NW, int MS> struct OpSel<ROWS, TT, KB, NW, true, MS> {
   KOperand<ROWS, KB, NW> ld;
   KFrag<TT, KB> fr;
 };
-template <int ROWS, int TT, int KB, int NW, bool MS> struct OpSel<ROWS, TT, KB, NW, false, MS> {
+template <int ROWS, int TT, int KB, int NW, int MS> struct OpSel<ROWS, TT, KB, NW, false, MS> {
   ROperand<ROWS, KB, NW, MS> ld;
   RFrag<TT, ROWS> fr;
 };
@@ -276,8 +304,8 @@ template <int ROWS, int TT, int KB, int NW, bool MS> struct OpSel<ROWS, TT, KB, 
 // ---- the kernel -----------------------------------------------------------
 // NS LDS stages of KB-deep slabs: slab kt+NS-1 is requested while slab kt is
 // multiplied, so global latency is hidden behind NS-1 slabs of MFMA work.
-// BMS: the B operand is row-contiguous with several segments along K.
-template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, int EPI, bool BMS>
+// BMS: segment mode of a row-contiguous B operand (ROperand's MS).
+template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, int EPI, int BMS>
 __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   constexpr int WGN = NW / 2;                  // waves along N (2 along M)
   constexpr int WM = BM / 2, WN = BN / WGN;
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   // loads: a wave blocks while its load instructions queue at the address
   // unit, and the other wave on the same SIMD keeps the matrix core fed.
   constexpr int NL = NW >= 8 ? NW / 2 : NW;    // waves that issue the loads
-  OpSel<BM, TM, KB, NL, AK, false> oa;
+  OpSel<BM, TM, KB, NL, AK, 0> oa;
   OpSel<BN, TN, KB, NL, BKC, BMS> ob;
   constexpr int LOADS = decltype(oa.ld)::NI + decltype(ob.ld)::NI;  // per slab
   oa.ld.init(g.a, m0, g.K, wave, lane);
@@ -338,7 +366,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   // Requests q0 .. q1-1 (of LOADS) of slab kt into stage dst.
   auto issue = [&](int kt, Q3L_LDS char* dst, int q0, int q1) __attribute__((always_inline)) {
     const bool last = kt == klast;
-#pragma unroll
+    // Fully unrolled whatever the code size: the loaders' per-lane offset
+    // arrays are then indexed by constants and stay in registers.
+#pragma clang loop unroll(full)
     for (int q = 0; q < LOADS; ++q) {
       if (q < q0 || q >= q1) continue;
       if (q < NIA)
@@ -597,7 +627,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, bool BMS = false>
+template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, int BMS = 0>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   dim3 grid(ntm * ntn), block(64 * NW);
@@ -622,9 +652,14 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
   // along K in an input-gradient GEMM) only.
   if (!ak && g.a.nseg > 1) return hipErrorInvalidValue;
   if (ak && bk) return launch_epi<BM, BN, KB, NS, NW, true, true>(g, s);
-  if (ak && !bk)
-    return g.b.nseg > 1 ? launch_epi<BM, BN, KB, NS, NW, true, false, true>(g, s)
-                        : launch_epi<BM, BN, KB, NS, NW, true, false>(g, s);
+  if (ak && !bk) {
+    if (g.b.nseg == 1) return launch_epi<BM, BN, KB, NS, NW, true, false>(g, s);
+    bool aligned = true;
+    for (int i = 1; i < g.b.nseg; ++i)
+      aligned = aligned && g.b.start[i] % KB == 0 && g.b.ld[i] == g.b.ld[0];
+    return aligned ? launch_epi<BM, BN, KB, NS, NW, true, false, 1>(g, s)
+                   : launch_epi<BM, BN, KB, NS, NW, true, false, 2>(g, s);
+  }
   if (!ak && !bk) {
     if (g.b.nseg > 1) return hipErrorInvalidValue;
     return launch_epi<BM, BN, KB, NS, NW, false, false>(g, s);
