@@ -83,6 +83,14 @@ __device__ inline f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b,
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
       0, 0);
 }
+// mfma16(a, b, c): the same for a 16x16x32 bf16 tile.  Lane l supplies
+// A[l%16][8*(l/16)+j] in a[j] and B[8*(l/16)+j][l%16] in b[j]; it receives
+// D[4*(l/16) + i][l%16] in d[i].
+__device__ inline f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
 
 // ---- wave reductions (wave64) ---------------------------------------------
 __device__ inline float wave_sum(float v) {
@@ -98,6 +106,15 @@ __device__ inline float group_sum(float v, int width) {
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) {
   return (a + b - 1) / b;
+}
+
+// Consecutive workgroup ids of a launch go round-robin to the 8 XCDs (each
+// with its own L2).  Renumbered so XCD x works through one contiguous range
+// of the nb logical ids, in order: the logical id of workgroup bid.
+__device__ inline int xcd_contiguous(int bid, int nb) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
 // ---- LDS: direct loads from global memory and transposing reads ----------

@@ -86,7 +86,11 @@ struct KOperand {
   static constexpr int RPW = 64 / CPRK;
   static constexpr int NI = R / (NW * RPW);  // wave-instructions per thread per slab
   uint32_t voff[NI];   // per lane: byte offset of its chunk at k0 = 0
-  uint32_t vtail[NI];  // the same for the last slab: kOOB where the chunk is past K
+  // For the last slab: kOOB where the lane's chunk is past K, else 0.  The
+  // chunk's swizzle, and so the chunk, is the same for every instruction of
+  // the lane (the rows they cover advance by a multiple of 16), so one mask
+  // serves all; voff < 2^31, so voff | kOOB is past the buffer's range.
+  uint32_t tmask;
   uint64_t base[NI];   // uniform: segment base of the instruction's rows
 
   __device__ void init(const Operand& o, int r0, int K, int wave, int lane) {
@@ -118,7 +122,7 @@ struct KOperand {
         if (gr > o.rows - 1) gr = o.rows - 1;
         voff[i] = (uint32_t)((int64_t)(gr - st) * ld * 2 + 16 * c);
       }
-      vtail[i] = (klast + 8 * c < K) ? voff[i] : kOOB;
+      if (i == 0) tmask = (klast + 8 * c < K) ? 0u : kOOB;
       base[i] = p;
     }
   }
@@ -128,7 +132,7 @@ struct KOperand {
   // the scalar offset.
   __device__ void issue_one(const Operand&, int i, int k0, int, bool last,
                             Q3L_LDS char* dst, int wave) const {
-    lds_dma16(base[i], last ? vtail[i] : voff[i], uni(2u * (uint32_t)k0),
+    lds_dma16(base[i], last ? voff[i] | tmask : voff[i], uni(2u * (uint32_t)k0),
           uni(lds_addr(dst + 1024 * (NW * i + wave))));
   }
 };
@@ -138,13 +142,19 @@ struct KOperand {
 // activations read along the token axis).  The tile sits in LDS as in
 // memory, [KB][R]: CPR 16-byte chunks per k-row; wave-instruction q fills
 // k-rows RPI*q ..; lane l writes k-row RPI*q + l/CPR, slot l%CPR, holding
-// global chunk slot ^ (4 * (krow & 3)).  Fragments are read with the gfx950
+// global chunk slot ^ rswz(krow).  Fragments are read with the gfx950
 // transposing LDS read, two 8-byte reads per fragment, at the byte rate of
 // the 16-byte reads (no bank conflicts).  Measured on the Qwen3-8B weight
 // gradients this form reaches 0.44-0.51 of the bf16 peak against 0.49-0.51
 // for the K-contiguous form on transposed copies, so the layer's backward
 // still transposes its operands once; this form serves the stand-alone
 // gradient entry points and the layer without transposed copies.
+// Chunk permutation of k-row kr of a row-contiguous tile: the transposing
+// fragment reads of 32 lanes cover k-rows {0..3, 8..11} (+16 j) at one pair
+// of chunks each, and the eight even values 2 ((kr & 3) | (kr & 8) >> 1)
+// put those rows' pairs on eight distinct 32-byte bank windows.
+__device__ inline int rswz(int kr) { return 2 * ((kr & 3) | ((kr >> 1) & 4)); }
+
 // MS: 0 one segment; 1 several segments along K, each starting at a
 // multiple of KB and all of one row stride (a slab lies in one segment);
 // 2 several segments in general.
@@ -165,7 +175,8 @@ struct ROperand {
   uint64_t vb1, vb2;              // uniform (MS 1): segment bases minus start * ld * 2
   int st1, st2;                   // uniform (MS 1): segment starts (past K if absent)
   int64_t ld0;                    // uniform: row stride (elements)
-  uint32_t voff[NI], vtail[NI];
+  uint32_t voff[NI];
+  int ktail;                      // klast + the lane's k-row in instruction 0
 
   __device__ void init(const Operand& o, int r0, int K, int wave, int lane) {
     base0 = uni64((uint64_t)o.p[0]);
@@ -184,24 +195,29 @@ struct ROperand {
       vb2 = n > 2 ? p2 - (uint64_t)((int64_t)s2 * ld0 * 2) : base0;
     }
     const int klast = (K - 1) / KB * KB;
+    ktail = klast + RPI * wave + lane / CPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = NW * i + wave;
       const int kr = RPI * q + lane / CPR;
-      const int c = (lane % CPR) ^ (4 * (kr & 3));
+      const int c = (lane % CPR) ^ rswz(kr);
       int n = r0 + 8 * c;
       if (n > o.rows - 8) n = o.rows - 8;
       col[i] = n;
       krl[i] = kr;
       voff[i] = (uint32_t)(((int64_t)kr * ld0 + n) * 2);
-      vtail[i] = klast + kr < K ? voff[i] : kOOB;
     }
+  }
+  // Offset of instruction i in the last slab: kOOB where its k-row (ktail +
+  // RPI NW i) is past K.
+  __device__ uint32_t tail(int i, int K) const {
+    return ktail + RPI * NW * i < K ? voff[i] : kOOB;
   }
   __device__ void issue_one(const Operand& o, int i, int k0, int K, bool last,
                             Q3L_LDS char* dst, int wave) const {
     const uint32_t lds = uni(lds_addr(dst + 1024 * (NW * i + wave)));
     if constexpr (MS == 0) {
-      lds_dma16(base0 + (uint64_t)((int64_t)k0 * ld0 * 2), last ? vtail[i] : voff[i], 0u, lds);
+      lds_dma16(base0 + (uint64_t)((int64_t)k0 * ld0 * 2), last ? tail(i, K) : voff[i], 0u, lds);
       return;
     }
     if constexpr (MS == 1) {
@@ -210,7 +226,7 @@ struct ROperand {
       const uint64_t m1 = 0ull - (uint64_t)(k0 >= st1), m2 = 0ull - (uint64_t)(k0 >= st2);
       const uint64_t vb = base0 + ((vb1 - base0) & m1) + ((vb2 - vb1) & m2);
       // (readfirstlane: the value is uniform, the compiler cannot tell)
-      lds_dma16(uni64(vb + (uint64_t)((int64_t)k0 * ld0 * 2)), last ? vtail[i] : voff[i], 0u,
+      lds_dma16(uni64(vb + (uint64_t)((int64_t)k0 * ld0 * 2)), last ? tail(i, K) : voff[i], 0u,
                 lds);
       return;
     }
@@ -232,12 +248,8 @@ struct ROperand {
 // ---- tile order -----------------------------------------------------------
 __device__ inline void map_tile(int bid, int nb, int ntm, int ntn, int& tm,
                                 int& tn) {
-  // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
-  // renumber so XCD x works on one contiguous range of logical tiles.
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int logical = (xcd < rem) ? xcd * (per + 1) + slot
-                                  : rem * (per + 1) + (xcd - rem) * per + slot;
+  // Each XCD works on one contiguous range of logical tiles.
+  const int logical = xcd_contiguous(bid, nb);
   constexpr int GM = 8;
   const int in_group = GM * ntn;
   const int group = logical / in_group;
@@ -253,10 +265,12 @@ __device__ inline float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f +
 __device__ inline float silu_f(float g) { return g * sigmoid_f(g); }
 
 // ---- fragment readers -----------------------------------------------------
-// K-contiguous tile [rows][KB]: lane reads row wb + 32*i + lane%32, k-chunk
-// 2*kk + lane/32 (swizzled).  Addresses: lane base + per-kk offset + i*32 rows.
+// Two matrix-instruction shapes are used (see the kernel): 32x32x16 where
+// both operands are K-contiguous, 16x16x32 where one is row-contiguous.
+// 32x32x16, K-contiguous tile [rows][KB]: lane reads row wb + 32 i + l%32,
+// k-chunk 2 kk + l/32 (swizzled); k-steps are 16 deep.
 template <int TT, int KB>
-struct KFrag {
+struct KFrag32 {
   uint32_t base;
   uint32_t koff[KB / 16];
   __device__ void init(int wb, int lane) {
@@ -269,33 +283,55 @@ struct KFrag {
     return ld_lds16(t + base + koff[kk] + 64 * KB * i);
   }
 };
-// Row-contiguous tile [KB][R] (row stride 2R bytes), transposed reads: in
-// 16-lane group g, lane s points at k-row 8*(g/2) + s/4 (+4 for the second
-// read), columns wb + 32*i + 16*(g%2) + 4*(s%4) .. +3 (chunks swizzled by
-// 4 * (k-row & 3)).
+// 16x16x32: lane l holds rows (or columns) 16 i + l%16 of the wave's block i
+// and k = 8 (l/16) .. +7 of k-step kk (32 deep).  K-contiguous tile
+// [rows][KB]: lane reads row wb + 16 i + l%16, chunk 4 kk + l/16 (swizzled;
+// the swizzle of a 16-row block repeats, so it depends on l%16 only).
+template <int TT, int KB>
+struct KFrag16 {
+  uint32_t base;
+  uint32_t koff[KB / 32];
+  __device__ void init(int wb, int lane) {
+    const int r = wb + (lane & 15), g = lane >> 4, sw = kswz<KB>(lane & 15);
+    base = (uint32_t)r * (2 * KB);
+#pragma unroll
+    for (int kk = 0; kk < KB / 32; ++kk) koff[kk] = (uint32_t)(((4 * kk + g) ^ sw) << 4);
+  }
+  __device__ u32x4_t read(const Q3L_LDS char* t, int kk, int i) const {
+    return ld_lds16(t + base + koff[kk] + 32 * KB * i);
+  }
+};
+// Row-contiguous tile [KB][R] (row stride 2R bytes), transposing reads: in
+// 16-lane group g, source lane s points at k-row 8 g + s/4 (+4 for the second
+// read) of the k-step, columns wb + 16 i + 4 (s%4) .. +3; the transposing
+// read hands output lane s the four k values of column wb + 16 i + s.
 template <int TT, int R>
 struct RFrag {
   uint32_t base[TT];
   __device__ void init(int wb, int lane) {
-    const int g = (lane >> 4) & 3, sl = lane & 15;
-    const uint32_t rowoff = (uint32_t)(8 * (g >> 1) + (sl >> 2)) * (2 * R) + 8 * (sl & 1);
+    const int g = lane >> 4, sl = lane & 15;
+    const int kr = 8 * g + (sl >> 2);
+    const uint32_t rowoff = (uint32_t)kr * (2 * R) + 8 * (sl & 1);
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-      const int chunk = (((wb + 32 * i) >> 3) ^ (4 * (sl >> 2))) | (2 * (g & 1) + ((sl & 3) >> 1));
-      base[i] = rowoff + (uint32_t)chunk * 16u;
+      const int chunk = ((wb + 16 * i) >> 3) + ((sl & 3) >> 1);
+      base[i] = rowoff + (uint32_t)(chunk ^ rswz(kr)) * 16u;
     }
   }
   __device__ u32x4_t read(const Q3L_LDS char* t, int kk, int i) const {
-    return ld_tr_pair(t + base[i] + kk * 16 * (2 * R), 4 * (2 * R));
+    return ld_tr_pair(t + base[i] + kk * 32 * (2 * R), 4 * (2 * R));
   }
 };
 
-template <int ROWS, int TT, int KB, int NW, bool KC, int MS> struct OpSel;
-template <int ROWS, int TT, int KB, int NW, int MS> struct OpSel<ROWS, TT, KB, NW, true, MS> {
+template <int ROWS, int TT, int KB, int NW, bool KC, int MS, int MI> struct OpSel;
+template <int ROWS, int TT, int KB, int NW, int MS, int MI>
+struct OpSel<ROWS, TT, KB, NW, true, MS, MI> {
   KOperand<ROWS, KB, NW> ld;
-  KFrag<TT, KB> fr;
+  std::conditional_t<MI == 32, KFrag32<TT, KB>, KFrag16<TT, KB>> fr;
 };
-template <int ROWS, int TT, int KB, int NW, int MS> struct OpSel<ROWS, TT, KB, NW, false, MS> {
+template <int ROWS, int TT, int KB, int NW, int MS, int MI>
+struct OpSel<ROWS, TT, KB, NW, false, MS, MI> {
+  static_assert(MI == 16, "row-contiguous operands use the 16x16x32 shape");
   ROperand<ROWS, KB, NW, MS> ld;
   RFrag<TT, ROWS> fr;
 };
@@ -309,12 +345,22 @@ template <int BM, int BN, int KB, int NS, int NW, bool AK, bool BKC, int EPI, in
 __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   constexpr int WGN = NW / 2;                  // waves along N (2 along M)
   constexpr int WM = BM / 2, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
+  // Matrix-instruction shape.  v_mfma_f32_16x16x32_bf16 sustains more of the
+  // peak than v_mfma_f32_32x32x16_bf16 when two waves feed it, but one wave
+  // alone keeps it only half busy, so every stall of a SIMD's other wave
+  // costs more.  Measured on the layer's GEMMs: 32x32x16 where both operands
+  // are K-contiguous (the loader wave stalls at every slab), 16x16x32 where
+  // one is read with the transposing loads (the input gradients: 0.53-0.56
+  // of the peak against 0.50-0.52).
+  constexpr int MI = (AK && BKC) ? 32 : 16;
+  constexpr int TM = WM / MI, TN = WN / MI;   // MI x MI accumulator blocks
+  using Acc = std::conditional_t<MI == 32, f32x16_t, f32x4_t>;
+  constexpr int AEL = MI == 32 ? 16 : 4;      // accumulator elements per lane
   constexpr int ABYTES = BM * KB * 2, BBYTES = BN * KB * 2;
   constexpr int STAGE = ABYTES + BBYTES;
   // The epilogue reuses the LDS: per wave, the fp32 results of one pass
   // (rows padded by 16 bytes).  A wave's rows are staged in two passes, or
-  // one 32-row block per pass when it holds an odd number of blocks.
+  // 32 rows per pass when it holds an odd number of 32-row blocks.
   constexpr int ERS = (BN / (NW / 2)) * 4 + 16;      // staged row, bytes
   constexpr int EPASS = (BM / 64) % 2 == 0 ? 2 : BM / 64;
   constexpr int EREG = (BM / 2 / EPASS) * ERS;        // per wave
@@ -334,24 +380,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   // loads: a wave blocks while its load instructions queue at the address
   // unit, and the other wave on the same SIMD keeps the matrix core fed.
   constexpr int NL = NW >= 8 ? NW / 2 : NW;    // waves that issue the loads
-  OpSel<BM, TM, KB, NL, AK, 0> oa;
-  OpSel<BN, TN, KB, NL, BKC, BMS> ob;
+  OpSel<BM, TM, KB, NL, AK, 0, MI> oa;
+  OpSel<BN, TN, KB, NL, BKC, BMS, MI> ob;
   constexpr int LOADS = decltype(oa.ld)::NI + decltype(ob.ld)::NI;  // per slab
   oa.ld.init(g.a, m0, g.K, wave, lane);
   ob.ld.init(g.b, n0, g.K, wave, lane);
   oa.fr.init(wm * WM, lane);
   ob.fr.init(wn * WN, lane);
 
-  f32x16_t acc[TM][TN];
+  Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < AEL; ++e) acc[i][j][e] = 0.0f;
 
-  constexpr int KS = KB / 16;                  // k-steps per slab
-  static_assert(KS % 2 == 0 && NS >= 2, "slab pipeline shape");
+  constexpr int KS = KB / (MI == 32 ? 16 : 32);   // k-steps per slab
+  static_assert(NS >= 2 && (MI == 16 || KS % 2 == 0), "slab pipeline shape");
   // A slab's requests are spread over SP k-steps: with three or more stages
   // over a whole slab's worth of steps, with two (no slack) all at once.
   constexpr int SP = NS >= 3 ? KS : 1;
@@ -377,31 +423,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
         ob.ld.issue_one(g.b, q - NIA, kt * KB, g.K, last, dst + ABYTES, wave);
     }
   };
-  // Fragment read x of a k-step, in the order the matrix instructions
-  // consume them (row-major over the TM x TN accumulators): a0, b0 ..
-  // b{TN-1}, a1 .. a{TM-1}.
-  auto frag = [&](const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk, int x,
-                  u32x4_t (&af)[TM], u32x4_t (&bf)[TN]) __attribute__((always_inline)) {
-    if (x == 0)
-      af[0] = oa.fr.read(As, kk, 0);
-    else if (x <= TN)
-      bf[x - 1] = ob.fr.read(Bs, kk, x - 1);
-    else
-      af[x - TN] = oa.fr.read(As, kk, x - TN);
-  };
-  // One k-step in a fixed order of NM slots: slot x holds matrix
-  // instruction x, then (if rd) fragment read x of the next step, then (if
+  // Fragments.  32x32x16: double-buffered (par in use, par ^ 1 filling),
+  // read in the order the matrix instructions consume them.  16x16x32 (twice
+  // the instructions and fragments per k-step): held once, each replaced by
+  // the next step's right after its last matrix instruction (A'[i] after row
+  // i, B'[j] after the last row's instruction j).
+  constexpr int NBUF = MI == 32 ? 2 : 1;
+  u32x4_t af[NBUF][TM], bfr[NBUF][TN];
+  // One k-step in a fixed order of NM slots, row-major over the TM x TN
+  // accumulators: slot x holds matrix instruction x (B as the first operand,
+  // so each lane ends up with four consecutive output columns of one row),
+  // then (if rd) the next step's fragment reads due in that slot, then (if
   // ld) the x-th share of request part `part`.  Nothing moves across slots:
   // a request stalled at the address unit delays only what follows it, and
   // the other wave on the SIMD keeps the matrix core busy meanwhile.
-  auto step = [&](const u32x4_t (&ca)[TM], const u32x4_t (&cb)[TN], bool rd,
-                  const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk,
-                  u32x4_t (&na)[TM], u32x4_t (&nb)[TN], bool ld, int kt,
-                  Q3L_LDS char* dst, int part) __attribute__((always_inline)) {
+  auto step = [&](int par, bool rd, const Q3L_LDS char* As, const Q3L_LDS char* Bs, int kk,
+                  bool ld, int kt, Q3L_LDS char* dst, int part) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
-      acc[x / TN][x % TN] = mfma32(cb[x % TN], ca[x / TN], acc[x / TN][x % TN]);
-      if (rd && x < NF) frag(As, Bs, kk, x, na, nb);
+      const int i = x / TN, j = x % TN;
+      if constexpr (MI == 32) {
+        acc[i][j] = mfma32(bfr[par][j], af[par][i], acc[i][j]);
+        if (rd && x < NF) {
+          if (x == 0)
+            af[par ^ 1][0] = oa.fr.read(As, kk, 0);
+          else if (x <= TN)
+            bfr[par ^ 1][x - 1] = ob.fr.read(Bs, kk, x - 1);
+          else
+            af[par ^ 1][x - TN] = oa.fr.read(As, kk, x - TN);
+        }
+      } else {
+        acc[i][j] = mfma16(bfr[0][j], af[0][i], acc[i][j]);
+        if (rd) {
+          if (j == TN - 1) af[0][i] = oa.fr.read(As, kk, i);
+          if (i == TM - 1) bfr[0][j] = ob.fr.read(Bs, kk, j);
+        }
+      }
       if (ld) issue(kt, dst, part * NV + x * NV / NM, part * NV + (x + 1) * NV / NM);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -414,11 +471,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   }
   wait_vmcnt<LOADS * (NS - 1)>();
   stage_barrier();
-  // Fragments are double-buffered in registers: while the matrix cores work
-  // on k-step kk, the reads for step kk+1 are in flight.
-  u32x4_t af[2][TM], bfr[2][TN];
+  // While the matrix cores work on k-step kk, the reads for step kk+1 are in
+  // flight.
 #pragma unroll
-  for (int x = 0; x < NF; ++x) frag(lds, lds + ABYTES, 0, x, af[0], bfr[0]);
+  for (int i = 0; i < TM; ++i) af[0][i] = oa.fr.read(lds, 0, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bfr[0][j] = ob.fr.read(lds + ABYTES, 0, j);
 
   // The stage barrier sits before the LAST k-step of a slab, whose fragments
   // are already in registers: after it the next slab's first fragments are
@@ -441,25 +499,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
       const Q3L_LDS char* Bs = As + ABYTES;
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk)
-        step(af[kk & 1], bfr[kk & 1], true, As, Bs, kk + 1, af[(kk + 1) & 1],
-             bfr[(kk + 1) & 1], LD && kk + 1 < SP, pend, pend_dst, kk + 1);
+        step(kk & 1, true, As, Bs, kk + 1, LD && kk + 1 < SP, pend, pend_dst, kk + 1);
       wait_vmcnt<LOADS * (NS - 2)>();
       stage_barrier();
       const Q3L_LDS char* Nx = lds + nxt * STAGE;
       pend = min(kt + NS, klast);
       pend_dst = As;
-      step(af[(KS - 1) & 1], bfr[(KS - 1) & 1], true, Nx, Nx + ABYTES, 0, af[0], bfr[0], LD,
-           pend, pend_dst, 0);
+      step((KS - 1) & 1, true, Nx, Nx + ABYTES, 0, LD, pend, pend_dst, 0);
       cur = nxt;
     }
     const Q3L_LDS char* As = lds + cur * STAGE;
     const Q3L_LDS char* Bs = As + ABYTES;
 #pragma unroll
-    for (int kk = 0; kk < KS - 1; ++kk)
-      step(af[kk & 1], bfr[kk & 1], true, As, Bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1],
-           false, 0, nullptr, 0);
-    step(af[(KS - 1) & 1], bfr[(KS - 1) & 1], false, As, Bs, 0, af[0], bfr[0], false, 0,
-         nullptr, 0);
+    for (int kk = 0; kk < KS - 1; ++kk) step(kk & 1, true, As, Bs, kk + 1, false, 0, nullptr, 0);
+    step((KS - 1) & 1, false, As, Bs, 0, false, 0, nullptr, 0);
   };
   if (wave < NL)
     main_loop(std::true_type{});
@@ -470,21 +523,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
   wait_vmcnt<0>();
 
   // ---- epilogue ----
-  // Lane holds C[m][n..n+3] for each (i, j, q): m = i*32 + lane%32 and
-  // n = j*32 + 8q + 4*(lane/32) within the wave's WM x WN sub-tile.
+  // Lane holds C[m][n..n+3] for each (i, j, q) within the wave's WM x WN
+  // sub-tile: 32x32x16: m = i*32 + lane%32, n = j*32 + 8q + 4*(lane/32),
+  // q < 4; 16x16x32: m = i*16 + lane%16, n = j*16 + 4*(lane/16), q = 0.
   const Epilogue& e = g.epi;
-  const int hl = 4 * (lane >> 5);
+  constexpr int NQ = MI == 32 ? 4 : 1;
+  const int hl = MI == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
+  const int lr = lane & (MI - 1);
+  auto quad = [&](int i, int j, int q) __attribute__((always_inline)) {
+    if constexpr (MI == 32)
+      return f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                     acc[i][j][4 * q + 3]};
+    else
+      return acc[i][j];
+  };
   if constexpr (EPI == EPI_SILU_BWD) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WM + i * 32 + (lane & 31);
+      const int m = m0 + wm * WM + i * MI + lr;
       if (m >= g.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WN + j * 32 + 8 * q + hl;
+        for (int q = 0; q < NQ; ++q) {
+          const int n = n0 + wn * WN + j * MI + 8 * q + hl;
           if (n >= g.N) continue;
+          const f32x4_t cq = quad(i, j, q);
           const bf16_t* G = static_cast<const bf16_t*>(e.r) + (int64_t)m * e.ldr + n;
           const u32x2_t g2 = ld8(G), u2 = ld8(G + e.ffn);
           const float gg[4] = {lo_f(g2[0]), hi_f(g2[0]), lo_f(g2[1]), hi_f(g2[1])};
@@ -492,7 +556,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
           float dg[4], du[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float v = acc[i][j][4 * q + r];
+            const float v = cq[r];
             const float sg = sigmoid_f(gg[r]);
             dg[r] = v * uu[r] * sg * (1.0f + gg[r] * (1.0f - sg));
             du[r] = v * gg[r] * sg;
@@ -512,8 +576,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     // wave's LDS accesses execute in order, so a pass may overwrite the
     // region right after the previous pass's reads.
     static_assert((WN == 64 || WN == 128) && TM % EPASS == 0, "epilogue staging shape");
-    constexpr int BPP = TM / EPASS;            // 32-row blocks per pass
-    constexpr int PR = 32 * BPP;               // rows per pass
+    constexpr int BPP = TM / EPASS;            // MI-row blocks per pass
+    constexpr int PR = MI * BPP;               // rows per pass
     constexpr int LPR = WN / 4;                // lanes per staged row (4 floats each)
     constexpr int RPT = 64 / LPR;              // staged rows per read
     constexpr int NT = PR / RPT;               // reads per pass (plain epilogues)
@@ -558,12 +622,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x16_t& c = acc[pass * BPP + ii][j];
-            *reinterpret_cast<Q3L_LDS f32x4_t*>(
-                reg + (ii * 32 + (lane & 31)) * ERS + (j * 32 + 8 * q + hl) * 4) =
-                f32x4_t{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
-          }
+          for (int q = 0; q < NQ; ++q)
+            *reinterpret_cast<Q3L_LDS f32x4_t*>(reg + (ii * MI + lr) * ERS +
+                                                (j * MI + 8 * q + hl) * 4) =
+                quad(pass * BPP + ii, j, q);
       if constexpr (EPI == EPI_SILU_MUL) {
         // Staged row: per 64-column block bb, g in columns 64 bb + 0..31
         // and u in 64 bb + 32..63 (the paired operand interleaves 32-column
