@@ -107,7 +107,7 @@ def phase_work(c: dict) -> tuple:
         "B3 gate/up wgrad gemm": ("mfma", 2 * T * 2 * f * d),
         "B4 rmsnorm bwd": norm_bwd,
         "B5 o dgrad gemm": ("mfma", 2 * T * d * qd),
-        "B5 o wgrad transposes": ("hbm", 2 * a * T * (d + qd)),
+        "B5 o wgrad transposes": ("hbm", 0),   # none: both operands read in place
         "B5 o wgrad gemm": ("mfma", 2 * T * d * qd),
         "B6 attention bwd": ("mfma", 8 * c["h_q"] * dh * pairs),
         "B7 qk-norm + rope bwd": ("hbm", 3 * a * T * nqk + 4 * T * heads),
