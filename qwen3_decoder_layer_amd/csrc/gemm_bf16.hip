@@ -568,6 +568,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
       }
     }
   } else {
+    // Results that the next kernels do not read right away leave with
+    // non-temporal stores (streamed past the caches' retention): 40 us less
+    // per layer step across the plain, partial-sum and weight-gradient
+    // epilogues.  The SwiGLU output is the down projection's next operand and
+    // keeps ordinary stores (non-temporal there cost that GEMM 4%).
+    auto st8n = [](void* p, u32x2_t v) __attribute__((always_inline)) {
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+    };
     // Staged through LDS: once every wave is past its last fragment read,
     // each wave writes its fp32 sub-tile one pass (half, or a third) at a
     // time into its own LDS region and reads it back row-major, so every global access covers
@@ -663,15 +671,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
               v[0] += lo_f(rr[pass][t][0]); v[1] += hi_f(rr[pass][t][0]);
               v[2] += lo_f(rr[pass][t][1]); v[3] += hi_f(rr[pass][t][1]);
             }
-            st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
-                u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
+            st8n(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
+                 u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
           } else if constexpr (EPI == EPI_PARTIAL) {
-            *reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + nn) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + nn));
             if (resid) {
               const u32x2_t r2 = rr[pass][t];
-              st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
-                  u32x2_t{pack2(v[0] + lo_f(r2[0]), v[1] + hi_f(r2[0])),
-                          pack2(v[2] + lo_f(r2[1]), v[3] + hi_f(r2[1]))});
+              st8n(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
+                   u32x2_t{pack2(v[0] + lo_f(r2[0]), v[1] + hi_f(r2[0])),
+                           pack2(v[2] + lo_f(r2[1]), v[3] + hi_f(r2[1]))});
             }
           } else if constexpr (EPI == EPI_WGRAD) {
             const bool s1 = wg_nseg > 1 && m >= wg_st1;
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
             Q3L_GLOBAL f32x4_t* C = reinterpret_cast<Q3L_GLOBAL f32x4_t*>(
                 cb + ((uint64_t)(m - cst) * e.ldc + nn) * 4);
             if (e.accumulate) v += *C;
-            *C = v;
+            __builtin_nontemporal_store(v, C);
           }
         }
       }
