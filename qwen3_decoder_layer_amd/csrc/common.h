@@ -176,8 +176,20 @@ __device__ inline u32x4_t buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// Cache-policy bit of a buffer access: non-temporal (streamed past the
+// caches' retention).
+constexpr int kNT = 2;
+template <int AUX = 0>
 __device__ inline void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+__device__ inline u32x2_t buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <int AUX = 0>
+__device__ inline void buf_st8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(
+      __builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off, 0, AUX);
 }
 
 template <int N>

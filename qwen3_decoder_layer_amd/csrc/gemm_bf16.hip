@@ -573,9 +573,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     // per layer step across the plain, partial-sum and weight-gradient
     // epilogues.  The SwiGLU output is the down projection's next operand and
     // keeps ordinary stores (non-temporal there cost that GEMM 4%).
-    auto st8n = [](void* p, u32x2_t v) __attribute__((always_inline)) {
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
-    };
     // Staged through LDS: once every wave is past its last fragment read,
     // each wave writes its fp32 sub-tile one pass (half, or a third) at a
     // time into its own LDS region and reads it back row-major, so every global access covers
@@ -591,16 +588,45 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     constexpr int NT = PR / RPT;               // reads per pass (plain epilogues)
     Q3L_LDS char* reg = lds + wave * EREG;
     const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+    // Global accesses go through buffer resources that start at the wave's
+    // first row and end at row M (or after the wave's rows): a lane's byte
+    // offset is fixed per matrix and advances by a multiple of the row
+    // stride per staged row, rows past M fall outside the resource (loads
+    // read zeros, stores are dropped), and a lane whose columns lie past N
+    // gets an offset past every resource.  No 64-bit address arithmetic per
+    // row.  Results that the next kernels do not read right away leave with
+    // non-temporal stores (streamed past the caches' retention); the SwiGLU
+    // output, the down projection's next operand, keeps ordinary stores.
+    // (The resource fields are uniform; uni() lets the compiler keep them in
+    // scalar registers instead of looping over lanes.)
+    const int vrows = (int)uni((uint32_t)max(0, min(g.M - mw, WM)));   // the wave's rows inside M
+    auto rsrc_rows = [&](const void* base, int64_t ld, int esz) __attribute__((always_inline)) {
+      const uint64_t b = uni64((uint64_t)(static_cast<const char*>(base) + (int64_t)mw * ld * esz));
+      return buf_rsrc(reinterpret_cast<const void*>(b), uni((uint32_t)((int64_t)vrows * ld * esz)));
+    };
     // Plain epilogues: in pass p, lane reads staged row RPT t + lane / LPR
     // (t < NT), columns 4 (lane % LPR) .. +3.  The bf16 residual they add is
-    // requested for every pass before the first barrier, at addresses
-    // clamped into the matrix where the tile overhangs it, so the loads
+    // requested for every pass before the first barrier, so the loads
     // overlap one another and the staging instead of each waiting in turn.
-    const int cn = 4 * (lane % LPR), nn = nw + cn;
-    const int nclamp = nn < g.N ? nn : g.N - 4;
-    const bf16_t* resid = nullptr;
-    if constexpr (EPI == EPI_STORE) resid = static_cast<const bf16_t*>(e.r);
-    if constexpr (EPI == EPI_PARTIAL) resid = e.c ? static_cast<const bf16_t*>(e.r) : nullptr;
+    const int cn = 4 * (lane % LPR), nn = nw + cn, rl = lane / LPR;
+    const bool colok = nn < g.N;
+    auto loff = [&](int64_t ld, int esz) __attribute__((always_inline)) {
+      return colok ? (uint32_t)(((int64_t)rl * ld + nn) * esz) : kOOB;
+    };
+    // Byte offset of staged row (pass, t) relative to the lane's first row.
+    auto roff = [&](int pass, int t, int64_t ld, int esz) __attribute__((always_inline)) {
+      return (uint32_t)((int64_t)(pass * PR + RPT * t) * ld * esz);
+    };
+    const void* resid = nullptr;
+    if constexpr (EPI == EPI_STORE) resid = e.r;
+    if constexpr (EPI == EPI_PARTIAL) resid = e.c ? e.r : nullptr;
+    __amdgpu_buffer_rsrc_t rres = buf_rsrc(nullptr, 0), rc = rres, rp = rres;
+    uint32_t ores = 0, oc = 0, op = 0;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
+      if (resid) { rres = rsrc_rows(resid, e.ldr, 2); ores = loff(e.ldr, 2); }
+      if (e.c) { rc = rsrc_rows(e.c, e.ldc, 2); oc = loff(e.ldc, 2); }
+      if constexpr (EPI == EPI_PARTIAL) { rp = rsrc_rows(e.p32, e.ldp, 4); op = loff(e.ldp, 4); }
+    }
     u32x2_t rr[EPASS][NT];
     // Weight-gradient output segments, read once into registers: selecting
     // among fields of the argument block per lane would make the compiler
@@ -609,16 +635,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
     const int wg_st1 = (int)uni((uint32_t)e.cstart[1]), wg_st2 = (int)uni((uint32_t)e.cstart[2]);
     const uint64_t wg_c0 = uni64((uint64_t)e.cs[0]), wg_c1 = uni64((uint64_t)e.cs[1]),
                    wg_c2 = uni64((uint64_t)e.cs[2]);
+    // Weight gradients: output rows split into up to three segments.  When
+    // the wave's rows lie in one of them (no segment starts inside them),
+    // one resource over that segment serves every row; otherwise each row
+    // picks its segment.
+    bool wone = false;
+    __amdgpu_buffer_rsrc_t rw = rres;
+    uint32_t ow = 0;
+    if constexpr (EPI == EPI_WGRAD) {
+      const int sg = (wg_nseg > 2 && mw >= wg_st2) ? 2 : (wg_nseg > 1 && mw >= wg_st1) ? 1 : 0;
+      const int sst = sg == 2 ? wg_st2 : sg == 1 ? wg_st1 : 0;
+      const int snext = (sg == 0 && wg_nseg > 1) ? wg_st1 : (sg == 1 && wg_nseg > 2) ? wg_st2 : INT_MAX;
+      wone = mw + vrows <= snext;
+      const uint64_t cb = sg == 2 ? wg_c2 : sg == 1 ? wg_c1 : wg_c0;
+      const uint64_t b = uni64(cb + (uint64_t)((int64_t)(mw - sst) * e.ldc * 4));
+      rw = buf_rsrc(reinterpret_cast<const void*>(b), uni((uint32_t)((int64_t)vrows * e.ldc * 4)));
+      ow = loff(e.ldc, 4);
+    }
     if constexpr (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
       if (resid) {
 #pragma unroll
         for (int pass = 0; pass < EPASS; ++pass)
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            int m = mw + pass * PR + RPT * t + lane / LPR;
-            if (m > g.M - 1) m = g.M - 1;
-            rr[pass][t] = ld8(resid + (int64_t)m * e.ldr + nclamp);
-          }
+          for (int t = 0; t < NT; ++t)
+            rr[pass][t] = buf_ld8(rres, ores + roff(pass, t, e.ldr, 2));
       }
     }
     stage_barrier();
@@ -637,7 +677,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
       if constexpr (EPI == EPI_SILU_MUL) {
         // Staged row: per 64-column block bb, g in columns 64 bb + 0..31
         // and u in 64 bb + 32..63 (the paired operand interleaves 32-column
-        // blocks); f column = nw / 2 + 32 bb + c.
+        // blocks); f column = nw / 2 + 32 bb + c.  Lane: staged row
+        // 8 (t / (WN / 64)) + lane / 8, columns 4 (lane % 8) .. +3 of block
+        // t % (WN / 64).
+        const __amdgpu_buffer_rsrc_t rf = rsrc_rows(e.c, e.ldc, 2);
+        const __amdgpu_buffer_rsrc_t rg = rsrc_rows(e.gu, e.gu ? e.ldgu : 0, 2);
 #pragma unroll
         for (int t = 0; t < PR * (WN / 64) / 8; ++t) {
           const int bb = t % (WN / 64), row = 8 * (t / (WN / 64)) + (lane >> 3);
@@ -646,17 +690,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
               *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 256 * bb + 4 * c);
           const f32x4_t uv =
               *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 256 * bb + 128 + 4 * c);
-          const int m = mp + row, f = nw / 2 + 32 * bb + c;
-          if (m >= g.M || f >= e.ffn) continue;
+          const int f = nw / 2 + 32 * bb + c;
+          const int r = pass * PR + row;        // row within the wave's rows
           float fv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) fv[r] = silu_f(gv[r]) * uv[r];
-          st8(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + f,
-              u32x2_t{pack2(fv[0], fv[1]), pack2(fv[2], fv[3])});
+          for (int x = 0; x < 4; ++x) fv[x] = silu_f(gv[x]) * uv[x];
+          const bool fok = f < e.ffn;
+          buf_st8(rf, fok ? (uint32_t)(((int64_t)r * e.ldc + f) * 2) : kOOB,
+                  u32x2_t{pack2(fv[0], fv[1]), pack2(fv[2], fv[3])});
           if (e.gu) {
-            bf16_t* G = static_cast<bf16_t*>(e.gu) + (int64_t)m * e.ldgu + f;
-            st8(G, u32x2_t{pack2(gv[0], gv[1]), pack2(gv[2], gv[3])});
-            st8(G + e.ffn, u32x2_t{pack2(uv[0], uv[1]), pack2(uv[2], uv[3])});
+            const uint32_t og = fok ? (uint32_t)(((int64_t)r * e.ldgu + f) * 2) : kOOB;
+            buf_st8(rg, og, u32x2_t{pack2(gv[0], gv[1]), pack2(gv[2], gv[3])});
+            buf_st8(rg, og + (uint32_t)(e.ffn * 2), u32x2_t{pack2(uv[0], uv[1]), pack2(uv[2], uv[3])});
           }
         }
       } else {
@@ -664,24 +709,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const GemmArgs g) {
         for (int t = 0; t < NT; ++t) {
           const int row = RPT * t + lane / LPR;
           f32x4_t v = *reinterpret_cast<const Q3L_LDS f32x4_t*>(reg + row * ERS + 4 * cn);
-          const int m = mp + row;
-          if (m >= g.M || nn >= g.N) continue;
           if constexpr (EPI == EPI_STORE) {
             if (resid) {
               v[0] += lo_f(rr[pass][t][0]); v[1] += hi_f(rr[pass][t][0]);
               v[2] += lo_f(rr[pass][t][1]); v[3] += hi_f(rr[pass][t][1]);
             }
-            st8n(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
-                 u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
+            buf_st8<kNT>(rc, oc + roff(pass, t, e.ldc, 2),
+                         u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
           } else if constexpr (EPI == EPI_PARTIAL) {
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(e.p32 + (int64_t)m * e.ldp + nn));
+            buf_st16<kNT>(rp, op + roff(pass, t, e.ldp, 4), __builtin_bit_cast(u32x4_t, v));
             if (resid) {
               const u32x2_t r2 = rr[pass][t];
-              st8n(static_cast<bf16_t*>(e.c) + (int64_t)m * e.ldc + nn,
-                   u32x2_t{pack2(v[0] + lo_f(r2[0]), v[1] + hi_f(r2[0])),
-                           pack2(v[2] + lo_f(r2[1]), v[3] + hi_f(r2[1]))});
+              buf_st8<kNT>(rc, oc + roff(pass, t, e.ldc, 2),
+                           u32x2_t{pack2(v[0] + lo_f(r2[0]), v[1] + hi_f(r2[0])),
+                                   pack2(v[2] + lo_f(r2[1]), v[3] + hi_f(r2[1]))});
             }
           } else if constexpr (EPI == EPI_WGRAD) {
+            if (wone) {
+              const uint32_t o = ow + roff(pass, t, e.ldc, 4);
+              if (e.accumulate) v += __builtin_bit_cast(f32x4_t, buf_ld16(rw, o));
+              buf_st16<kNT>(rw, o, __builtin_bit_cast(u32x4_t, v));
+              continue;
+            }
+            const int m = mp + row;
+            if (m >= g.M || nn >= g.N) continue;
             const bool s1 = wg_nseg > 1 && m >= wg_st1;
             const bool s2 = wg_nseg > 2 && m >= wg_st2;
             const uint64_t cb = s2 ? wg_c2 : (s1 ? wg_c1 : wg_c0);
