@@ -52,17 +52,20 @@ namespace {
 // Segment holding index idx of an operand (idx uniform): base pointer, ld
 // (elements) and start.  Every field is read from the kernel argument through
 // readfirstlane before the select, so the compiler keeps the choice between
-// register values instead of folding it into an indexed load of the table.
+// register values instead of folding it into an indexed load of the table;
+// the fields of unused segments are read too (never selected), so the reads
+// are unconditional and shared by every call.
 __device__ inline void pick(const Operand& o, int idx, uint64_t& p, int64_t& ld, int& st) {
   const int n = (int)uni((uint32_t)o.nseg);
-  const int s1 = n > 1 ? (int)uni((uint32_t)o.start[1]) : 0x7fffffff;
-  const int s2 = n > 2 ? (int)uni((uint32_t)o.start[2]) : 0x7fffffff;
+  const int s1r = (int)uni((uint32_t)o.start[1]), s2r = (int)uni((uint32_t)o.start[2]);
+  const int s1 = n > 1 ? s1r : 0x7fffffff;
+  const int s2 = n > 2 ? s2r : 0x7fffffff;
   const uint64_t p0 = uni64((uint64_t)o.p[0]);
-  const uint64_t p1 = uni64((uint64_t)o.p[n > 1 ? 1 : 0]);
-  const uint64_t p2 = uni64((uint64_t)o.p[n > 2 ? 2 : 0]);
+  const uint64_t p1 = uni64((uint64_t)o.p[1]);
+  const uint64_t p2 = uni64((uint64_t)o.p[2]);
   const int64_t l0 = (int64_t)uni64((uint64_t)o.ld[0]);
-  const int64_t l1 = (int64_t)uni64((uint64_t)o.ld[n > 1 ? 1 : 0]);
-  const int64_t l2 = (int64_t)uni64((uint64_t)o.ld[n > 2 ? 2 : 0]);
+  const int64_t l1 = (int64_t)uni64((uint64_t)o.ld[1]);
+  const int64_t l2 = (int64_t)uni64((uint64_t)o.ld[2]);
   const bool b1 = idx >= s1, b2 = idx >= s2;
   p = b2 ? p2 : (b1 ? p1 : p0);
   ld = b2 ? l2 : (b1 ? l1 : l0);
@@ -95,36 +98,45 @@ struct KOperand {
 
   __device__ void init(const Operand& o, int r0, int K, int wave, int lane) {
     const int klast = (K - 1) / KB * KB;
+    const int rows = (int)uni((uint32_t)o.rows);
+    // One branch on the layout (uniform), then straight-line code per
+    // instruction.
+    auto each = [&](auto paired) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int q = NW * i + wave;
-      const int row = RPW * q + lane / CPRK;
-      const int c = (lane % CPRK) ^ kswz<KB>(row);
-      int gr = r0 + row;
-      uint64_t p;
-      int64_t ld;
-      int st;
-      if (o.paired) {
-        const int g0 = r0 + RPW * q;        // uniform: first logical row
-        const bool up = (g0 >> 5) & 1;
-        const uint64_t pg = uni64((uint64_t)o.p[0]), pu = uni64((uint64_t)o.p[1]);
-        const int64_t lg = (int64_t)uni64((uint64_t)o.ld[0]);
-        const int64_t lu = (int64_t)uni64((uint64_t)o.ld[1]);
-        p = up ? pu : pg;
-        ld = up ? lu : lg;
-        int pr = (gr >> 6) * 32 + (gr & 31);
-        if (pr >= o.rows) pr = o.rows - 1;
-        voff[i] = (uint32_t)((int64_t)pr * ld * 2 + 16 * c);
-      } else {
-        int g0 = r0 + RPW * q;
-        if (g0 > o.rows - 1) g0 = o.rows - 1;
-        pick(o, g0, p, ld, st);
-        if (gr > o.rows - 1) gr = o.rows - 1;
-        voff[i] = (uint32_t)((int64_t)(gr - st) * ld * 2 + 16 * c);
+      for (int i = 0; i < NI; ++i) {
+        const int q = NW * i + wave;
+        const int row = RPW * q + lane / CPRK;
+        const int c = (lane % CPRK) ^ kswz<KB>(row);
+        int gr = r0 + row;
+        uint64_t p;
+        int64_t ld;
+        int st;
+        if constexpr (decltype(paired)::value) {
+          const int g0 = r0 + RPW * q;        // uniform: first logical row
+          const bool up = (g0 >> 5) & 1;
+          const uint64_t pg = uni64((uint64_t)o.p[0]), pu = uni64((uint64_t)o.p[1]);
+          const int64_t lg = (int64_t)uni64((uint64_t)o.ld[0]);
+          const int64_t lu = (int64_t)uni64((uint64_t)o.ld[1]);
+          p = up ? pu : pg;
+          ld = up ? lu : lg;
+          int pr = (gr >> 6) * 32 + (gr & 31);
+          if (pr >= rows) pr = rows - 1;
+          voff[i] = (uint32_t)((int64_t)pr * ld * 2 + 16 * c);
+        } else {
+          int g0 = r0 + RPW * q;
+          if (g0 > rows - 1) g0 = rows - 1;
+          pick(o, g0, p, ld, st);
+          if (gr > rows - 1) gr = rows - 1;
+          voff[i] = (uint32_t)((int64_t)(gr - st) * ld * 2 + 16 * c);
+        }
+        if (i == 0) tmask = (klast + 8 * c < K) ? 0u : kOOB;
+        base[i] = p;
       }
-      if (i == 0) tmask = (klast + 8 * c < K) ? 0u : kOOB;
-      base[i] = p;
-    }
+    };
+    if (uni((uint32_t)o.paired))
+      each(std::true_type{});
+    else
+      each(std::false_type{});
   }
   // Wave-instruction i of the slab starting at k0, into LDS stage `dst`
   // (R * KB * 2 bytes); `last` (uniform) selects the offsets that zero-fill
@@ -785,7 +797,9 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
     if (g.b.nseg > 1) return hipErrorInvalidValue;
     return launch_epi<BM, BN, KB, NS, NW, false, false>(g, s);
   }
-  return launch_epi<BM, BN, KB, NS, NW, false, true>(g, s);
+  // A row-contiguous with B K-contiguous: no caller forms it (the weight
+  // gradients take both operands in one form), so it is not instantiated.
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -61,7 +61,9 @@ struct GemmArgs {
 };
 
 // bf16 MFMA GEMM (K must be a multiple of 8; every k_contig = 0 operand's
-// rows a multiple of 8).
+// rows a multiple of 8).  Operand forms: both K-contiguous, A K-contiguous
+// with B row-contiguous, or both row-contiguous; A row-contiguous with B
+// K-contiguous returns hipErrorInvalidValue.
 hipError_t gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Plain fp32 GEMM with the same argument structure (correctness path).
 hipError_t gemm_f32(const GemmArgs& g, hipStream_t s);
