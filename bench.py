@@ -43,10 +43,10 @@ COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 # --kernel-probe`, each scaled by what the same counter reads for the 1 GiB
 # calibration copy.  Valid only for the kernel source it was taken on: the
 # digest below is of gemm_bf16.hip, and a changed source reports null.
-TRAFFIC = {"source_sha256": "1312639ac1d64e23",
-           "fetch_kib": 1180825.0, "write_kib": 590462.9,
-           "copy_fetch_kib": 524303.1, "copy_write_kib": 1048576.0,
-           "bytes": 3022893748}
+TRAFFIC = {"source_sha256": "308dc6e7f6ecf8b2",
+           "fetch_kib": 1181332.7, "write_kib": 592372.0,
+           "copy_fetch_kib": 524303.0, "copy_write_kib": 1048576.0,
+           "bytes": 3025889103}
 
 WORKLOADS = {
     "qwen3-8b-bf16-fwd-bwd": 4,
@@ -244,7 +244,8 @@ def dominant_work(T: int, d: int, f: int) -> tuple:
 def kernel_probe(cfg: dict) -> None:
     """Short run for hardware-counter passes: a plain 1 GiB device copy (the
     calibration kernel: reads and writes exactly COPY_BYTES), then the
-    dominant kernel, each a few times."""
+    dominant kernel, each a few times, then one training forward and one
+    backward of the layer on one stream (every kernel of a step once)."""
     import torch
     import qwen3_decoder_layer_amd as q3
     lc = q3.LayerConfig.from_dict(cfg)
@@ -259,8 +260,20 @@ def kernel_probe(cfg: dict) -> None:
     stream = torch.cuda.current_stream()
     ms = time_dominant(lc, gate, up, stream, 5)
     torch.cuda.synchronize()
-    print(f"kernel probe: copy {COPY_BYTES} B x3, dominant kernel {ms:.3f} ms avg",
-          flush=True)
+    del gate, up
+    inp = synth.make_inputs(cfg, 1000 + 5, with_dy=True)
+    W = {n: torch.from_numpy(inp[n]).to(dev, torch.bfloat16) for n in synth.PARAM_NAMES}
+    x = torch.from_numpy(inp["x"]).to(dev, torch.bfloat16)
+    dy = torch.from_numpy(inp["dy"]).to(dev, torch.bfloat16)
+    saved = torch.empty(q3.saved_bytes(lc), dtype=torch.uint8, device=dev)
+    ws = torch.empty(q3.workspace_bytes(lc, True), dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty(W[n].shape, dtype=torch.float32, device=dev) for n in W}
+    q3.layer_forward(lc, W, x, saved=saved, stream=stream)
+    q3.layer_backward(lc, W, x, dy, saved, dx=dx, grads=grads, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    print(f"kernel probe: copy {COPY_BYTES} B x3, dominant kernel {ms:.3f} ms avg, "
+          "then one layer step", flush=True)
 
 
 def split_probe(cfg: dict) -> None:
@@ -391,23 +404,35 @@ def main():
     ms = res["elapsed"] / args.steps * 1e3
     tflops = fl["total"] / (ms * 1e-3) / 1e12
     fwd_work, bwd_work = phase_work(cfg)
+    # The time between two of the library's marks also holds one gap between
+    # the mark and the next kernel (the event's packet and the launch, about
+    # 5 us here), which a kernel trace of the same phase does not count.  A
+    # phase without kernels measures exactly that gap, so every phase time
+    # below is its mark time less the median time of the run's empty phases
+    # (kept as "ms_marks"), i.e. its kernels' time.
+    empty = [t for times, work in ((res["fwd_phase_ms"], fwd_work),
+                                   (res["bwd_phase_ms"], bwd_work))
+             for name, t in times.items() if work[name][1] == 0]
+    gap = float(np.median(empty)) if empty else 0.0
     phases = []
     for times, work in ((res["fwd_phase_ms"], fwd_work), (res["bwd_phase_ms"], bwd_work)):
-        for name, t in times.items():
+        for name, tm in times.items():
             bound, amount = work[name]
             if name == "transposes for the backward" and cfg["backward"]:
                 continue   # on the second stream, beside F5: no time of its own
+            t = tm - gap
             if amount == 0 or t <= 0:
                 continue
             if bound == "mfma":
                 ach, peak, unit = amount / (t * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
             else:
                 ach, peak, unit = amount / (t * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-            phases.append({"phase": name, "ms": round(float(t), 4), "bound": bound,
+            phases.append({"phase": name, "ms": round(float(t), 4),
+                           "ms_marks": round(float(tm), 4), "bound": bound,
                            "work": int(amount), "achieved": round(float(ach), 1),
                            "unit": unit, "frac": round(float(ach / peak), 4)})
     dom = "F8-F9 gate/up gemm + swiglu"
-    k_ms = float(res["fwd_phase_ms"][dom])
+    k_ms = float(res["fwd_phase_ms"][dom]) - gap
     k_flops, k_bytes = dominant_work(T, cfg["d"], cfg["d_ffn"])
     k_tflops = k_flops / (k_ms * 1e-3) / 1e12
     line = {
@@ -439,10 +464,12 @@ def main():
                      "frac": k_tflops / PEAK_BF16_TFLOPS,
                      "avg_ms": k_ms,
                      "timing": "median over the steps of the launch inside the step, "
-                               "between HIP events the library records on its stream",
+                               "between HIP events the library records on its stream, "
+                               "less the mark-to-kernel gap (phase_gap_ms)",
                      "algorithmic_bytes": k_bytes,
                      "traffic": traffic_bytes()},
         "phases": phases,
+        "phase_gap_ms": round(gap, 4),
         "marked_ms_per_step": res["marked_elapsed"] / args.steps * 1e3,
     }
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
