@@ -548,8 +548,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 // are added through LDS at the end.  K and V of the workgroup's keys and
 // double-buffered Q / dO tiles sit in LDS in the layout above, filled by
 // direct global->LDS loads (no registers, no LDS store instructions); the
-// transposed operands of dV^T += dO^T P^T and dK^T += Q^T dS^T come from
-// transposing LDS reads of the same tiles.
+// wave's K fragments, the same for every query tile, are also held in
+// registers (one LDS read per score instruction instead of two; V's would
+// not fit beside them at two waves per SIMD); the transposed operands of
+// dV^T += dO^T P^T and dK^T += Q^T dS^T come from transposing LDS reads of
+// the same tiles.
 template <int DH>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   constexpr int NKK = DH / 16, NDT = DH / 32;
@@ -624,6 +627,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dkt[dt][e] = 0.f; dvt[dt][e] = 0.f; }
+  // The wave's K fragments are the same for every query tile: read once.
+  u32x4_t kfr[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    kfr[kk] = ld_lds16((const Q3L_LDS void*)(uintptr_t)(kbase ^ (uint32_t)(32 * kk)));
 
   for (int it = 0; it < total; ++it) {
     const int s = it & 1;
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
         const int o = j >= NKK;
         const uint32_t x = (uint32_t)(32 * (j - NKK * o));
         fa = lds16((qb ^ x) + (uint32_t)(TB * o));     // Q or dO
-        fb = lds16((kb ^ x) + (uint32_t)(KVB * o));    // K or V
+        if (o) fb = lds16((kb ^ x) + (uint32_t)KVB);   // V (K is in kfr)
       };
       const int qr0 = 32 * half + 4 * h;               // row of element 0 in the tile
       constexpr int EP = 16 / NKK;                     // exponentials per dP slot
@@ -672,7 +680,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           if (j < NKK)
-            sc = mfma32(ra[j % 3], rb[j % 3], sc);
+            sc = mfma32(ra[j % 3], kfr[j], sc);
           else
             dp = mfma32(ra[j % 3], rb[j % 3], dp);
           if (j + 2 < NS) frags(j + 2, ra[(j + 2) % 3], rb[(j + 2) % 3]);
