@@ -674,16 +674,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
       f32x4_t l4;
       {
         constexpr int NS = 2 * NKK;
-        u32x4_t ra[3], rb[3];
+        u32x4_t ra[4], rb[4];
         frags(0, ra[0], rb[0]);
         frags(1, ra[1], rb[1]);
+        frags(2, ra[2], rb[2]);
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           if (j < NKK)
-            sc = mfma32(ra[j % 3], kfr[j], sc);
+            sc = mfma32(ra[j % 4], kfr[j], sc);
           else
-            dp = mfma32(ra[j % 3], rb[j % 3], dp);
-          if (j + 2 < NS) frags(j + 2, ra[(j + 2) % 3], rb[(j + 2) % 3]);
+            dp = mfma32(ra[j % 4], rb[j % 4], dp);
+          if (j + 3 < NS) frags(j + 3, ra[(j + 3) % 4], rb[(j + 3) % 4]);
           if (j >= NKK) {
 #pragma unroll
             for (int x = 0; x < EP; ++x) {
@@ -719,18 +720,19 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
         auto trf = [&](int j) __attribute__((always_inline)) {
           return TrOffsets<DH>::read_x(tb, j < 2 * NDT ? (uint32_t)TB : 0u, (j / NDT) % 2, j % NDT);
         };
-        u32x4_t rt[3];
+        u32x4_t rt[4];
         rt[0] = trf(0);
         rt[1] = trf(1);
+        rt[2] = trf(2);
         u32x4_t df[2];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const int hk = (j / NDT) % 2, dt = j % NDT;
           if (j < 2 * NDT)
-            dvt[dt] = mfma32(rt[j % 3], pf[hk], dvt[dt]);
+            dvt[dt] = mfma32(rt[j % 4], pf[hk], dvt[dt]);
           else
-            dkt[dt] = mfma32(rt[j % 3], df[hk], dkt[dt]);
-          if (j + 2 < NT) rt[(j + 2) % 3] = trf(j + 2);
+            dkt[dt] = mfma32(rt[j % 4], df[hk], dkt[dt]);
+          if (j + 3 < NT) rt[(j + 3) % 4] = trf(j + 3);
           if (j < 2 * NDT) {
 #pragma unroll
             for (int x = 0; x < DP; ++x) {
