@@ -99,11 +99,11 @@ def phase_work(c: dict) -> tuple:
     }
     bwd = {
         "B1 down dgrad gemm": ("mfma", 2 * T * d * f),
-        "B2 swiglu adjoint": ("hbm", 8 * a * T * f),
+        "B2 swiglu adjoint": ("hbm", 7 * a * T * f),
         "B1 down wgrad transposes": ("hbm", 2 * a * T * d),
         "B1 down wgrad gemm": ("mfma", 2 * T * d * f),
         "B3 gate/up dgrad gemm": ("mfma", 2 * T * 2 * f * d),
-        "B3 gate/up wgrad transposes": ("hbm", 2 * a * T * d),
+        "B3 gate/up wgrad transposes": ("hbm", 0),   # none: hn read in place
         "B3 gate/up wgrad gemm": ("mfma", 2 * T * 2 * f * d),
         "B4 rmsnorm bwd": norm_bwd,
         "B5 o dgrad gemm": ("mfma", 2 * T * d * qd),

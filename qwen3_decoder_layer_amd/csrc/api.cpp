@@ -144,10 +144,10 @@ struct BwdWs {
   // gradients (separate, so an input-gradient-only call leaves both for the
   // weight-gradient call that follows it).
   size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart_post, wpart_in, qpart, kpart;
-  // bf16 only: three scratch buffers for the transposed operands of the
-  // weight-gradient GEMMs ([features, Tp]).  (The transposed weights are in
-  // the saved block.)
-  size_t tA, tB, tC;
+  // bf16 only: two scratch buffers for the transposed operands of the
+  // weight-gradient GEMMs ([features, Tp]): [dg du]^T, then [dq dk dv]^T
+  // (tA), and dy^T (tC).
+  size_t tA, tC;
   size_t total;
 };
 
@@ -173,7 +173,6 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
   if (c.dtype == Q3L_BF16) {
     const size_t Tp = (size_t)pad8(m.T);
     w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
-    w.tB = take((size_t)std::max<int64_t>(std::max<int64_t>(m.ffn, m.qd), m.d) * Tp * 2);
     w.tC = take((size_t)m.d * Tp * 2);
   }
   w.total = off;
@@ -627,30 +626,41 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   const int Tp = (int)pad8(m.T);
   const char* xnt = bt ? at(saved, L.xnt) : nullptr;
   char* tA = bt ? at(workspace, W.tA) : nullptr;
-  char* tB = bt ? at(workspace, W.tB) : nullptr;
   char* tC = bt ? at(workspace, W.tC) : nullptr;
   // Weight gradient dW[ma, nb] (+)= sum_t A[t, ma] B[t, nb] (ma, nb are
   // feature counts; A/B activations with row strides lda/ldb), as two
-  // phases: the operand transposes (bf16: A into ta, B into tb, skipping
-  // those marked done; one launch) and the GEMM.
-  // copy = false reads both operands in place with the transposing loads
-  // (row-contiguous form): as fast as the transposed copies for the o
-  // projection's 4096 x 4096 gradient, 13-20% slower for the larger ones.
+  // phases: the operand transposes (bf16; one launch, skipping those marked
+  // done) and the GEMM.  Forms (bf16; the fp32 path reads both in place):
+  //   kCopies  both operands transposed to [features, Tp] copies, read
+  //            K-contiguous (32x32x16 instructions);
+  //   kACopy   A transposed, B read in place with the transposing LDS loads
+  //            (the input-gradient form, 16x16x32 instructions);
+  //   kInPlace both read in place.
+  // Measured on the layer's shapes: kACopy is 2-5% faster than kCopies for
+  // the down and gate/up gradients and saves B's copy, kCopies is 10% faster
+  // for the QKV gradient (its 192-row tiles fill the CUs), and kInPlace
+  // matches kCopies for the o gradient without any copy.
+  enum WForm { kCopies, kACopy, kInPlace };
   auto wgrad = [&](int phase_t, const void* A, int lda, int ma, const void* B, int ldb,
                    int nb, Epilogue e, char* ta, char* tb, bool a_done,
-                   bool b_done, bool copy) -> hipError_t {
+                   bool b_done, WForm form) -> hipError_t {
     GemmArgs g{};
-    if (bt && copy) {
+    if (bt && form != kInPlace) {
       TransposeJob jobs[2];
       int nj = 0;
       if (!a_done) jobs[nj++] = TransposeJob{A, lda, ta, Tp, T, Tp, ma};
-      if (!b_done) jobs[nj++] = TransposeJob{B, ldb, tb, Tp, T, Tp, nb};
+      if (form == kCopies && !b_done) jobs[nj++] = TransposeJob{B, ldb, tb, Tp, T, Tp, nb};
       hipError_t err = transpose_bf16_batch(jobs, nj, s);
       if (err != hipSuccess) return err;
       if ((err = mk.end(phase_t)) != hipSuccess) return err;
       g.a = kop(ta, Tp, ma);
-      g.b = kop(tb, Tp, nb);
-      g.K = Tp;
+      if (form == kCopies) {
+        g.b = kop(tb, Tp, nb);
+        g.K = Tp;
+      } else {
+        g.b = rop(B, ldb, nb);
+        g.K = T;
+      }
     } else {
       const hipError_t err = mk.end(phase_t);
       if (err != hipSuccess) return err;
@@ -667,8 +677,8 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
 
   // Step 9 (down_proj): df = dy W_down.  fp32: fused with the SwiGLU adjoint
   // in the GEMM epilogue.  bf16: df lands in the dg half of dgu, and a
-  // separate pass turns it into dg | du, writing the transposes the two
-  // weight gradients read as well: [dg du]^T and f^T (an epilogue that reads
+  // separate pass turns it into dg | du, writing the transposed copy the
+  // gate/up weight gradient reads as well: [dg du]^T (an epilogue that reads
   // g, u would hold the matrix cores idle while it waits on memory).
   if (chain) {
     GemmArgs g{};
@@ -687,15 +697,13 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   Q3L_HIP(mk.end(0));
   if (bt && chain)
     Q3L_HIP(swiglu_bwd_bf16(T, Tp, m.ffn, dgu, 2 * (int64_t)m.ffn, gu, 2 * (int64_t)m.ffn,
-                            dgu, 2 * (int64_t)m.ffn, want_w ? tA : nullptr, Tp,
-                            want_w ? tB : nullptr, s));
-  if (bt && deferred)   // [dg du]^T and f^T from the dg | du the INPUT call left
-    Q3L_HIP(swiglu_transposes_bf16(T, Tp, m.ffn, gu, 2 * (int64_t)m.ffn, dgu,
-                                   2 * (int64_t)m.ffn, tA, Tp, tB, s));
+                            dgu, 2 * (int64_t)m.ffn, want_w ? tA : nullptr, Tp, s));
+  if (bt && deferred)   // [dg du]^T from the dg | du the INPUT call left
+    Q3L_HIP(swiglu_transposes_bf16(T, Tp, m.ffn, dgu, 2 * (int64_t)m.ffn, tA, Tp, s));
   Q3L_HIP(mk.end(1));
-  if (want_w)  // dW_down = dy^T f  (bf16: f^T already in tB)
+  if (want_w)  // dW_down = dy^T f  (bf16: dy^T into tC, f read in place)
     Q3L_HIP(wgrad(2, dy, m.d, m.d, f, m.ffn, m.ffn, epi_wgrad(grads->down, m.ffn, acc), tC,
-                  tB, false, bt, true));
+                  nullptr, false, false, kACopy));
   Q3L_HIP(mk.end(3));
   // Step 9 (gate/up): dhn = dg W_gate + du W_up (one GEMM over stacked K).
   if (chain) {
@@ -708,10 +716,11 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     Q3L_HIP(gemm(dt, g, s));
   }
   Q3L_HIP(mk.end(4));
-  if (want_w) {  // dW_gate | dW_up = [dg du]^T hn  ([dg du]^T already in tA)
+  if (want_w) {  // dW_gate | dW_up = [dg du]^T hn  ([dg du]^T already in tA, hn in place)
     Epilogue e = epi_wgrad(grads->gate, m.d, acc);
     e.cs[1] = grads->up; e.cstart[1] = m.ffn; e.cnseg = 2;
-    Q3L_HIP(wgrad(5, dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e, tA, tB, bt, false, true));
+    Q3L_HIP(wgrad(5, dgu, 2 * m.ffn, 2 * m.ffn, hn, m.d, m.d, e, tA, nullptr, bt, false,
+                  kACopy));
   }
   Q3L_HIP(mk.end(6));
   // Steps 8 and 10: post-attention RMSNorm adjoint plus the residual dy.
@@ -732,8 +741,8 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   }
   Q3L_HIP(mk.end(8));
   if (want_w)  // dW_o = dh^T O, both operands read in place
-    Q3L_HIP(wgrad(9, dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc), tA, tB,
-                  false, false, false));
+    Q3L_HIP(wgrad(9, dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc), nullptr,
+                  nullptr, false, false, kInPlace));
   Q3L_HIP(mk.end(10));
   // Step 5: attention backward (P recomputed from the log-sum-exp).
   if (chain) {
@@ -778,7 +787,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     e.cs[2] = grads->v; e.cstart[2] = m.qd + m.kvd;
     e.cnseg = 3;
     Q3L_HIP(wgrad(14, dqkv, m.nqkv, m.nqkv, xn, m.d, m.d, e, tA, const_cast<char*>(xnt),
-                  false, bt, true));
+                  false, bt, kCopies));
   }
   Q3L_HIP(mk.end(15));
   // Step 1: input RMSNorm adjoint plus the attention residual dh.
@@ -1014,7 +1023,7 @@ q3l_status q3l_swiglu_bwd(int32_t dtype, int64_t M, int32_t N, const void* df, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == Q3L_BF16) {
     Q3L_HIP(swiglu_bwd_bf16((int)M, (int)pad8(M), N, df, N, gu, 2 * (int64_t)N, dgu,
-                            2 * (int64_t)N, nullptr, 0, nullptr, s));
+                            2 * (int64_t)N, nullptr, 0, s));
   } else {
     Q3L_HIP(swiglu_bwd_f32(M, N, static_cast<const float*>(df), N,
                            static_cast<const float*>(gu), 2 * (int64_t)N,

@@ -84,17 +84,15 @@ hipError_t transpose_bf16_batch(const TransposeJob* jobs, int n, hipStream_t s);
 
 // SwiGLU adjoint, bf16: from df [T, ffn] and the saved g|u [T, 2 ffn] write
 // dgu = [dg | du] ([T, 2 ffn]) and, if dguT is not null, its transpose dguT
-// ([2 ffn, Tp], columns t >= T zero).  If fT is not null, also writes fT = (silu(g) u)^T
-// ([ffn, Tp], same ld_t, columns t >= T zero).  df may alias the dg half of
-// dgu (same ld).  ffn and Tp multiples of 8.
+// ([2 ffn, Tp], columns t >= T zero).  df may alias the dg half of dgu (same
+// ld).  ffn and Tp multiples of 8.
 hipError_t swiglu_bwd_bf16(int T, int Tp, int ffn, const void* df, int64_t ld_df,
                            const void* gu, int64_t ld_gu, void* dgu, int64_t ld_dgu,
-                           void* dguT, int64_t ld_t, void* fT, hipStream_t s);
-// Only the transposed copies of the above, from a dgu an earlier
-// swiglu_bwd_bf16 wrote: bitwise the dguT and fT the fused form writes.
-hipError_t swiglu_transposes_bf16(int T, int Tp, int ffn, const void* gu, int64_t ld_gu,
-                                  const void* dgu, int64_t ld_dgu, void* dguT, int64_t ld_t,
-                                  void* fT, hipStream_t s);
+                           void* dguT, int64_t ld_t, hipStream_t s);
+// Only the transposed copy of the above, from a dgu an earlier
+// swiglu_bwd_bf16 wrote: bitwise the dguT the fused form writes.
+hipError_t swiglu_transposes_bf16(int T, int Tp, int ffn, const void* dgu, int64_t ld_dgu,
+                                  void* dguT, int64_t ld_t, hipStream_t s);
 // fp32 SwiGLU adjoint, dgu = [dg | du] from df and g | u.
 hipError_t swiglu_bwd_f32(int64_t M, int ffn, const float* df, int64_t ld_df, const float* gu,
                           int64_t ld_gu, float* dgu, int64_t ld_dgu, hipStream_t s);
