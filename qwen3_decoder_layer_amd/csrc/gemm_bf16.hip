@@ -16,10 +16,11 @@
 //  - An operand contiguous along its rows instead (a weight read as
 //    [in, out], activations read along the token axis) is also loaded
 //    straight into LDS, as it is in memory, and read with the gfx950
-//    transposing LDS read (ds_read_b64_tr_b16).  That read sustains about a
-//    third of ds_read_b128's byte rate, so the layer's backward transposes
-//    its GEMM operands once (transpose.hip) and uses the K-contiguous path;
-//    the transposed-read path serves the stand-alone gradient entry points.
+//    transposing LDS read (ds_read_b64_tr_b16), at the byte rate of the
+//    16-byte reads when its swizzle keeps the banks apart (below).  The
+//    layer's input gradients read the weights this way, and the down and
+//    gate/up weight gradients their activations (the other operand a
+//    transposed copy).
 //  - K-contiguous LDS tiles are [rows][KB] with the 16-byte chunks of row r XOR-swizzled
 //    by (r >> 1) & 7, so the 16-byte fragment reads of 16 consecutive rows
 //    hit 16 distinct bank groups.  Two LDS stages: the next slab streams in
@@ -157,10 +158,10 @@ struct KOperand {
 // global chunk slot ^ rswz(krow).  Fragments are read with the gfx950
 // transposing LDS read, two 8-byte reads per fragment, at the byte rate of
 // the 16-byte reads (no bank conflicts).  Measured on the Qwen3-8B weight
-// gradients this form reaches 0.44-0.51 of the bf16 peak against 0.49-0.51
-// for the K-contiguous form on transposed copies, so the layer's backward
-// still transposes its operands once; this form serves the stand-alone
-// gradient entry points and the layer without transposed copies.
+// gradients with BOTH operands in this form: 0.44-0.51 of the bf16 peak
+// against 0.49-0.51 on two transposed copies; with one operand a copy and
+// the other in this form, 0.49-0.59 (the o gradient reads both in place,
+// the down and gate/up gradients one).
 // Chunk permutation of k-row kr of a row-contiguous tile: the transposing
 // fragment reads of 32 lanes cover k-rows {0..3, 8..11} (+16 j) at one pair
 // of chunks each, and the eight even values 2 ((kr & 3) | (kr & 8) >> 1)
