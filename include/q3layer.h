@@ -469,10 +469,19 @@ q3l_status q3l_attention_finish(int32_t dtype, int32_t B, int32_t L,
 /* Its backward: dq, dk, dv (dtype) are written with the row strides of q, k,
  * v (ldq, ldk, ldv) -- a caller that passes strided views must give dq, dk,
  * dv buffers of the same strides -- from o (stride ldo), dout (stride
- * lddo) and lse.  P is recomputed from lse.  workspace:
+ * lddo) and lse.  P is recomputed from lse.  workspace: at least
  * q3l_attention_bwd_workspace_bytes(B, L, h_q) bytes of scratch (the row
- * sums of dout * o). */
+ * sums of dout * o).  bf16 with at least
+ * q3l_attention_bwd_stored_ds_workspace_bytes(B, L, h_q) bytes (the row
+ * sums plus dS for the causal triangle in 32 x 32 bf16 blocks, about
+ * B h_q L^2 bytes): the dK/dV kernel also stores dS = P (dP - D) and dQ =
+ * dS K / sqrt(d_h) is formed from it, instead of a second kernel that
+ * recomputes S and dP (the walkthrough page's backward section: each
+ * operator's local gradient; the same values, computed once).  The results
+ * are bitwise the same either way. */
 size_t q3l_attention_bwd_workspace_bytes(int32_t B, int32_t L, int32_t h_q);
+size_t q3l_attention_bwd_stored_ds_workspace_bytes(int32_t B, int32_t L,
+                                                   int32_t h_q);
 q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L,
                              int32_t h_q, int32_t h_kv, int32_t d_h,
                              const void *q, int64_t ldq, const void *k,

@@ -610,9 +610,11 @@ def _like_strided(t):
 
 
 def attention_bwd(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq=None, dk=None,
-                  dv=None, stream=None):
+                  dv=None, stream=None, stored_ds=True):
     """dq, dk, dv are written with q, k, v's row strides: by default they
-    are allocated with the same strides."""
+    are allocated with the same strides.  stored_ds: give the library the
+    workspace with which the bf16 backward stores dS and forms dQ from it
+    (False: the minimum, with which it recomputes S and dP for dQ)."""
     B, L = q.shape[0], q.shape[1]
     dq = _like_strided(q) if dq is None else dq
     dk = _like_strided(k) if dk is None else dk
@@ -621,7 +623,8 @@ def attention_bwd(q, k, v, o, dout, lse, h_q, h_kv, d_h, dq=None, dk=None,
         if a.stride() != b.stride() or a.shape != b.shape:
             raise ValueError(f"{name} must have the shape and strides of its input")
     lib = library()
-    n = lib.q3l_attention_bwd_workspace_bytes(B, L, h_q)
+    n = (lib.q3l_attention_bwd_stored_ds_workspace_bytes if stored_ds
+         else lib.q3l_attention_bwd_workspace_bytes)(B, L, h_q)
     ws = _bytes(n, q.device)
     _check(lib.q3l_attention_bwd(
         _code(q.dtype), B, L, h_q, h_kv, d_h, _p(q), q.stride(1), _p(k),

@@ -123,6 +123,7 @@ PROTOTYPES = {
                                     _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                     _vp, _vp]),
     "q3l_attention_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "q3l_attention_bwd_stored_ds_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "q3l_attention_fwd_block": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
                                           _vp, _i64, _vp, _i64, _vp, _i64, _i32,
                                           _i32, _vp, _vp, _vp, _vp]),

@@ -146,8 +146,8 @@ struct BwdWs {
   size_t dgu, dhn, dh, dO, delta, dqk, dqkv, dxn, wpart_post, wpart_in, qpart, kpart;
   // bf16 only: two scratch buffers for the transposed operands of the
   // weight-gradient GEMMs ([features, Tp]): [dg du]^T, then [dq dk dv]^T
-  // (tA), and dy^T (tC).
-  size_t tA, tC;
+  // (tA), and dy^T (tC); and the attention backward's dS blocks (ds).
+  size_t tA, tC, ds;
   size_t total;
 };
 
@@ -174,6 +174,7 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
     const size_t Tp = (size_t)pad8(m.T);
     w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
     w.tC = take((size_t)m.d * Tp * 2);
+    w.ds = take(attn_ds_bytes(m.B, m.L, m.hq));
   }
   w.total = off;
   return w;
@@ -744,7 +745,8 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     Q3L_HIP(wgrad(9, dh, m.d, m.d, ao, m.qd, m.qd, epi_wgrad(grads->o, m.qd, acc), nullptr,
                   nullptr, false, false, kInPlace));
   Q3L_HIP(mk.end(10));
-  // Step 5: attention backward (P recomputed from the log-sum-exp).
+  // Step 5: attention backward (P recomputed from the log-sum-exp; bf16:
+  // dQ formed from the dS that the dK/dV kernel stores).
   if (chain) {
     AttnArgs a{};
     a.B = m.B; a.L = m.L; a.h_q = m.hq; a.h_kv = m.hkv; a.d_h = m.dh;
@@ -756,6 +758,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.dq = dqk; a.dk = dqk + (size_t)m.qd * m.es;
     a.dv = dqkv + (size_t)(m.qd + m.kvd) * m.es;
     a.delta = delta;
+    a.ds = bt ? at(workspace, W.ds) : nullptr;
     Q3L_HIP(attn_bwd(dt, a, s));
   }
   Q3L_HIP(mk.end(11));
@@ -1133,6 +1136,11 @@ size_t q3l_attention_bwd_workspace_bytes(int32_t B, int32_t L, int32_t h_q) {
   return up((size_t)B * h_q * L * 4);
 }
 
+size_t q3l_attention_bwd_stored_ds_workspace_bytes(int32_t B, int32_t L, int32_t h_q) {
+  if (B <= 0 || L <= 0 || h_q <= 0) return 0;
+  return q3l_attention_bwd_workspace_bytes(B, L, h_q) + up(attn_ds_bytes(B, L, h_q));
+}
+
 q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, int32_t h_kv,
                              int32_t d_h, const void* q, int64_t ldq, const void* k,
                              int64_t ldk, const void* v, int64_t ldv, const void* o,
@@ -1161,6 +1169,9 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
   a.o = const_cast<void*>(o); a.ldo = ldo; a.lse = const_cast<float*>(lse);
   a.dout = dout; a.lddo = lddo; a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  if (dtype == Q3L_BF16 &&
+      workspace_bytes >= q3l_attention_bwd_stored_ds_workspace_bytes(B, L, h_q))
+    a.ds = at(workspace, q3l_attention_bwd_workspace_bytes(B, L, h_q));
   Q3L_HIP(attn_bwd(dtype, a, static_cast<hipStream_t>(stream)));
   return Q3L_OK;
 }

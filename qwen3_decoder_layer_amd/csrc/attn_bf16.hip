@@ -38,6 +38,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int KT = 64;        // keys per tile
 constexpr float kTau = 8.0f;  // rescale threshold (log2 units), see the forward
+#ifndef Q3L_DQ_STAGES
+#define Q3L_DQ_STAGES 3
+#endif
+constexpr int kDqStages = Q3L_DQ_STAGES;   // LDS stages of the dQ-from-dS kernel
+#ifndef Q3L_DQ_WAVES
+#define Q3L_DQ_WAVES 8
+#endif
+constexpr int kDqWaves = Q3L_DQ_WAVES;     // its waves per workgroup
 
 struct FwdP {
   int B, L, h_q, h_kv, G, hb, rb;
@@ -50,7 +58,10 @@ struct FwdP {
   // backward
   const bf16_t* dout; int64_t lddo;
   bf16_t* dq; bf16_t* dk; bf16_t* dv;
-  float* delta;   // written by the dQ kernel, read by dK/dV
+  float* delta;   // written by the dQ (or row-sum) kernel, read by dK/dV
+  // stored-dS form: the dS blocks of the causal triangle (bf16), ds_nt
+  // blocks per (sequence, q head); null for the recomputing form.
+  bf16_t* ds; int64_t ds_nt;
   // block state (forward over the keys [k_lo, k_hi) only; unnormalised)
   int k_lo, k_hi;
   float* m_out; float* l_out; float* acc; int64_t ld_acc;
@@ -553,7 +564,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
 // not fit beside them at two waves per SIMD); the transposed operands of
 // dV^T += dO^T P^T and dK^T += Q^T dS^T come from transposing LDS reads of
 // the same tiles.
-template <int DH>
+//
+// DS (the stored-dS form): each wave also writes its 32x32 blocks of dS
+// (bf16, as packed for the dK^T instructions) to the dS buffer, for the
+// dQ-from-dS kernel below.  A block (query block qb, key block kb; 32 rows
+// each, kb <= qb) sits at block index qb (qb + 1) / 2 + kb of its (sequence,
+// q head), 2 KB each.  Inside a block the lane holding key kl (0..31) and
+// half h stores its two 16-byte packs hk = 0, 1 (queries 16 hk + 4 h +
+// {0..3, 8..11}) at byte 16 (16 (kl / 4) + 8 hk + 4 h + kl % 4): each store
+// instruction fills eight whole 128-byte lines, and the transposing reads
+// that the dQ kernel makes of the block (32 lanes = 16 packs, both halves)
+// hit 32 distinct 8-byte bank pairs.
+template <int DH, bool DS>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   constexpr int NKK = DH / 16, NDT = DH / 32;
   constexpr int QT = 64, KB = 128;             // queries per tile, keys per workgroup
@@ -633,10 +655,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   for (int kk = 0; kk < NKK; ++kk)
     kfr[kk] = ld_lds16((const Q3L_LDS void*)(uintptr_t)(kbase ^ (uint32_t)(32 * kk)));
 
+  // Stored-dS form: the lane's byte offset inside a block (see above).
+  const uint32_t ds_off = 256u * (uint32_t)(l32 >> 2) + 64u * (uint32_t)h + 16u * (uint32_t)(l32 & 3);
+
   for (int it = 0; it < total; ++it) {
     const int s = it & 1;
     if (it + 1 < total) load_tile(it + 1, s ^ 1);
     const int qh0 = (qt_first + it % nqt) * QT + 32 * half;   // this wave's first row
+    __amdgpu_buffer_rsrc_t rds = buf_rsrc(nullptr, 0);
+    if constexpr (DS) {
+      // This block's 2 KB (none for rows past the sequence: stores dropped).
+      const int head = kvh * p.G + it / nqt;
+      const int64_t qb = qh0 / 32, kb = kw0 / 32;
+      const int64_t blk = (qb * (qb + 1) / 2 + kb) * (p.B * p.h_q) + (int64_t)b * p.h_q + head;
+      rds = buf_rsrc(p.ds + blk * 1024, qh0 < L ? 2048u : 0u);
+    }
     // Skip row blocks entirely before this wave's keys (all masked).
     // One block of 32 queries x 32 keys as a fixed sequence of slots, each
     // one matrix instruction plus a share of the vector work that does not
@@ -741,7 +774,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
                 l4 = *reinterpret_cast<const f32x4_t*>(&sLD[s][1][qr0 + 8 * (e >> 2)]);
               dp[e] = sc[e] * (dp[e] - l4[e & 3]);
             }
-            if (j == 2 * NDT - 1) { df[0] = pack_half(dp, 0); df[1] = pack_half(dp, 1); }
+            if (j == 2 * NDT - 1) {
+              df[0] = pack_half(dp, 0);
+              df[1] = pack_half(dp, 1);
+              if constexpr (DS) {
+                buf_st16<kNT>(rds, ds_off, df[0]);
+                buf_st16<kNT>(rds, ds_off + 128u, df[1]);
+              }
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -979,6 +1019,159 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
     }
 }
 
+// Row sums D = rowsum(dO * O) for the stored-dS form, where no dQ kernel
+// runs before dK/dV: one wave per 32 rows of one q head, each lane half
+// summing half of a row in the order the dQ kernel above uses (so both forms
+// read the same D).
+template <int DH>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p) {
+  constexpr int NKK = DH / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int b = blockIdx.x / p.h_q, head = blockIdx.x % p.h_q;
+  const int L = p.L;
+  const int qw0 = blockIdx.y * 128 + 32 * wave;
+  if (qw0 >= L) return;
+  const int qrow = qw0 + l32, qr = min(qrow, L - 1);
+  const int64_t tok0 = (int64_t)b * L;
+  const bf16_t* op = p.dout + (tok0 + qr) * p.lddo + (int64_t)head * DH + 8 * h;
+  const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
+  u32x4_t of[NKK], ov[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    of[kk] = ld16(op + 16 * kk);
+    ov[kk] = ld16(opo + 16 * kk);
+  }
+  float dlt = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
+  dlt += __shfl_xor(dlt, 32, 64);
+  if (h == 0 && qrow < L) p.delta[((int64_t)b * p.h_q + head) * L + qrow] = dlt;
+}
+
+// dQ from the stored dS: dQ^T += K^T dS^T over the key blocks at or before
+// each query block, with no recomputation of S or dP.  Grid and wave roles
+// as in the dQ kernel above (its accumulation order too: d block by d block,
+// 16-key steps in key order, the same transposed K fragments).  Per K tile
+// of KT keys the workgroup loads the tile (shared by its waves) and each
+// wave its two 32x32 dS blocks (4 KB, contiguous in the dS buffer), NST
+// stages deep, all by direct global->LDS loads.  The dS^T operand (lane =
+// query, eight keys) comes from transposing reads of a block as the dK/dV
+// kernel stored it: for 16-key step ks of a block, source lane sl of 16-lane
+// group g reads keys 16 ks + 4 (g / 2) + sl / 4 (+8 for the second read),
+// queries 16 (g % 2) + 4 (sl % 4) .. +3, i.e. the 8 bytes at
+// 1024 ks + 256 (g / 2) + 128 (g % 2) + 64 (sl % 2) + 16 (sl / 4) +
+// 8 ((sl / 2) % 2) (+512).  The kernel is bound by reading dS from HBM.
+template <int DH, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_dq_ds_kernel(const FwdP p) {
+  constexpr int NDT = DH / 32, RB = 2 * DH;
+  constexpr int TB = KT * RB;                  // one K tile
+  constexpr int WB = 4096;                     // a wave's two dS blocks
+  constexpr int SB = TB + NW * WB;             // one stage
+  constexpr int NI = TB / 1024 / NW + WB / 1024;   // load instructions per wave and tile
+  __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
+  Q3L_LDS char* lds = (Q3L_LDS char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uni((uint32_t)(tid >> 6));
+  const int l32 = lane & 31, h = lane >> 5;
+  const int ngroups = p.G / p.hb;
+  const int b = blockIdx.x / (p.h_kv * ngroups);
+  const int rem = blockIdx.x % (p.h_kv * ngroups);
+  const int kvh = rem / ngroups, hg = rem % ngroups;
+  const int QB = 32 * (NW / p.hb);
+  const int qtile = gridDim.y - 1 - blockIdx.y;
+  const int q0 = qtile * QB;
+  const int head = kvh * p.G + hg * p.hb + (wave % p.hb);
+  const int qw0 = q0 + 32 * (wave / p.hb);
+  const int L = p.L;
+  const int64_t tok0 = (int64_t)b * L;
+  const int qend = min(q0 + QB, L);
+  const int ntiles = (qend + KT - 1) / KT;
+  const int wave_last = min(qw0 + 31, L - 1);
+  const int my_tiles = qw0 < L ? wave_last / KT + 1 : 0;
+  const int qrow = qw0 + l32;
+  const int64_t qb = qw0 / 32;                 // this wave's query block
+  // dS blocks (qb, 0 ..) of this wave, contiguous.
+  const int64_t nbh = (int64_t)p.B * p.h_q;   // blocks between key blocks kb and kb + 1
+  const bf16_t* dsrow = p.ds + ((qb * (qb + 1) / 2) * nbh + (int64_t)b * p.h_q + head) * 1024;
+
+  auto stage = [&](int s) { return lds + s * SB; };
+  TileLoader<DH, KT, NW> kld;
+  kld.init(p.ldk, wave, lane);
+  auto load_tile = [&](int t, int s) {
+    kld.load(p.k, p.ldk, tok0, kvh * DH, t * KT, L, stage(s), wave);
+    // Blocks 2t, 2t + 1 while they are at or before the query block (zeros
+    // past it, never read).
+    const int64_t nb = t < my_tiles ? min<int64_t>(2, qb - 2 * t + 1) : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        buf_rsrc(dsrow + 2 * t * nbh * 1024,
+                 (uint32_t)(nb == 0 ? 0 : nb == 1 ? 2048 : nbh * 2048 + 2048));
+#pragma unroll
+    for (int j = 0; j < WB / 1024; ++j)
+      lds_dma16_r(r, 16u * (uint32_t)lane, (uint32_t)(1024 * (j & 1) + (j >> 1) * nbh * 2048),
+                  uni(lds_addr(stage(s) + TB + wave * WB + 1024 * j)));
+  };
+  TrOffsets<DH> tro;
+  tro.init(lane);
+  const int g = lane >> 4, sl = lane & 15;
+  const uint32_t dsl = 256u * (uint32_t)(g >> 1) + 128u * (uint32_t)(g & 1) +
+                       64u * (uint32_t)(sl & 1) + 16u * (uint32_t)(sl >> 2) +
+                       8u * (uint32_t)((sl >> 1) & 1);
+
+  f32x16_t dqt[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqt[dt][e] = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < ntiles) load_tile(i, i);
+  for (int t = 0; t < ntiles; ++t) {
+    const int s = t % NST;
+    // Tile t has landed (later tiles may still be in flight), then everyone's
+    // part of it; the stage read in iteration t - 1 is free for tile t + NST - 1.
+    if (t + NST - 2 < ntiles) wait_vmcnt<NI * (NST - 2)>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (t + NST - 1 < ntiles) load_tile(t + NST - 1, (t + NST - 1) % NST);
+    if (t < my_tiles) {
+      const Q3L_LDS char* sK = stage(s);
+      const uint32_t db = lds_addr(stage(s) + TB + wave * WB) + dsl;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (2 * t + c > qb) break;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const uint32_t a = db + 2048u * c + 1024u * k2;
+          const u32x2_t x0 = ld_tr8((const Q3L_LDS void*)(uintptr_t)a);
+          const u32x2_t x1 = ld_tr8((const Q3L_LDS void*)(uintptr_t)(a + 512u));
+          const u32x4_t df = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            dqt[dt] = mfma32(tro.read(sK, 2 * c + k2, dt), df, dqt[dt]);
+        }
+      }
+    }
+  }
+
+  if (qrow >= L) return;
+  const float sc = p.scale_log2 / kLog2e;
+  bf16_t* dp_ = p.dq + (tok0 + qrow) * p.ldq + (int64_t)head * DH;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * dt + 8 * j + 4 * h;
+      st8(dp_ + d, u32x2_t{pack2(dqt[dt][4 * j] * sc, dqt[dt][4 * j + 1] * sc),
+                           pack2(dqt[dt][4 * j + 2] * sc, dqt[dt][4 * j + 3] * sc)});
+    }
+}
+
 FwdP make_params(const AttnArgs& a) {
   FwdP p{};
   p.B = a.B; p.L = a.L; p.h_q = a.h_q; p.h_kv = a.h_kv;
@@ -994,6 +1187,8 @@ FwdP make_params(const AttnArgs& a) {
   p.dout = (const bf16_t*)a.dout; p.lddo = a.lddo;
   p.dq = (bf16_t*)a.dq; p.dk = (bf16_t*)a.dk; p.dv = (bf16_t*)a.dv;
   p.delta = a.delta;
+  p.ds = (bf16_t*)a.ds;
+  p.ds_nt = attn_ds_blocks(a.L);
   return p;
 }
 
@@ -1031,13 +1226,32 @@ hipError_t attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
   dim3 kgrid((unsigned)(p.B * p.h_kv), (unsigned)cdiv(p.L, 128));
   const int QB = 32 * p.rb;
   dim3 qgrid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
-  // dQ first: it also writes the row sums D that dK/dV reads.
+  if (p.ds) {
+    // Stored dS: the row sums D, then dK/dV (which also writes dS), then dQ
+    // from dS.
+    dim3 dgrid((unsigned)(p.B * p.h_q), (unsigned)cdiv(p.L, 128));
+    dim3 dsgrid(qgrid.x, (unsigned)cdiv(p.L, 32 * (kDqWaves / p.hb)));
+    if (a.d_h == 128) {
+      hipLaunchKernelGGL(attn_delta_kernel<128>, dgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_dkdv_kernel<128, true>), kgrid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((attn_dq_ds_kernel<128, kDqWaves, kDqStages>), dsgrid,
+                         dim3(64 * kDqWaves), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(attn_delta_kernel<64>, dgrid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((attn_dkdv_kernel<64, true>), kgrid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL((attn_dq_ds_kernel<64, kDqWaves, kDqStages>), dsgrid,
+                         dim3(64 * kDqWaves), 0, s, p);
+    }
+    return hipGetLastError();
+  }
+  // Recomputing form.  dQ first: it also writes the row sums D that dK/dV
+  // reads.
   if (a.d_h == 128) {
     hipLaunchKernelGGL(attn_dq_kernel<128>, qgrid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(attn_dkdv_kernel<128>, kgrid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<128, false>), kgrid, dim3(512), 0, s, p);
   } else {
     hipLaunchKernelGGL(attn_dq_kernel<64>, qgrid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(attn_dkdv_kernel<64>, kgrid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<64, false>), kgrid, dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }

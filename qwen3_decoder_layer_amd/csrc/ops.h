@@ -161,12 +161,25 @@ struct AttnArgs {
   const void* dout; int64_t lddo;
   void* dq; void* dk; void* dv;   // strides ldq / ldk / ldv
   float* delta;                   // [B, h_q, L] scratch
+  // bf16: attn_ds_bytes(B, L, h_q) bytes of scratch for the stored-dS form
+  // (dQ formed from dS written by the dK/dV kernel), or null to recompute
+  // S and dP for dQ instead.  Results are the same either way.
+  void* ds;
   // block state only: keys [k_lo, k_hi); m, l [B, h_q, L]; acc [B*L, ld_acc]
   int k_lo, k_hi;
   float* m_out; float* l_out; float* acc; int64_t ld_acc;
 };
 hipError_t attn_fwd(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t attn_bwd(int dtype, const AttnArgs& a, hipStream_t s);
+// 32x32 dS blocks of the causal triangle per (sequence, q head), and the
+// bytes of the stored-dS scratch.
+inline int64_t attn_ds_blocks(int L) {
+  const int64_t n = (L + 31) / 32;
+  return n * (n + 1) / 2;
+}
+inline size_t attn_ds_bytes(int B, int L, int h_q) {
+  return (size_t)B * h_q * (size_t)attn_ds_blocks(L) * 2048;
+}
 // Unnormalised block state (m, l, acc) of attention over keys [k_lo, k_hi).
 hipError_t attn_block(int dtype, const AttnArgs& a, hipStream_t s);
 // state (m, l, acc) := merge(state, state2) (in place); rows [B*L], heads h_q.

@@ -213,6 +213,20 @@ def test_attention_offset_range_is_checked(abi, lib):
     assert st == 2 and "2 GiB" in err(lib)
 
 
+def test_attention_stored_ds_workspace(lib):
+    # The stored-dS form's workspace: the row sums plus one 2 KB bf16 block
+    # per 32 x 32 block of the causal triangle, per (sequence, q head).
+    for B, L, hq in ((1, 1, 1), (2, 131, 4), (1, 4096, 32), (3, 64, 8)):
+        n = (L + 31) // 32
+        ds = B * hq * n * (n + 1) // 2 * 2048
+        base = lib.q3l_attention_bwd_workspace_bytes(B, L, hq)
+        full = lib.q3l_attention_bwd_stored_ds_workspace_bytes(B, L, hq)
+        assert base >= B * hq * L * 4
+        assert ds <= full - base < ds + 4096
+    assert lib.q3l_attention_bwd_stored_ds_workspace_bytes(0, 64, 8) == 0
+    assert lib.q3l_attention_bwd_stored_ds_workspace_bytes(1, 0, 8) == 0
+
+
 def test_version_and_missing_library_fails_loudly(abi, lib, monkeypatch):
     assert lib.q3l_version() >= 1
     # No fallback: without the built library the binding raises.

@@ -243,8 +243,9 @@ def _attn_check(dtype, q, k, v, do, o, lse, dq, dk, dv, local_dqk=True):
         assert_close(name, a2, r2, TOL[dtype], local=loc)
 
 
-def _attn_run(dtype, q, k, v, do):
-    """Attention forward + backward on guarded, poisoned outputs."""
+def _attn_run(dtype, q, k, v, do, stored_ds=True):
+    """Attention forward + backward on guarded, poisoned outputs (bf16:
+    the stored-dS form, or with stored_ds=False the recomputing one)."""
     B, L, hq, dh = q.shape
     hkv = k.shape[2]
     gq = dev(q.reshape(B, L, hq * dh), dtype)
@@ -256,9 +257,14 @@ def _attn_run(dtype, q, k, v, do):
     dq = Guarded((B, L, hq * dh), _td(dtype))
     dk, dv = Guarded((B, L, hkv * dh), _td(dtype)), Guarded((B, L, hkv * dh), _td(dtype))
     q3.attention_bwd(gq, gk, gv, o.t, dev(do.reshape(B, L, hq * dh), dtype), lse.t, hq, hkv,
-                     dh, dq=dq.t, dk=dk.t, dv=dv.t)
+                     dh, dq=dq.t, dk=dk.t, dv=dv.t, stored_ds=stored_ds)
     dq.check("dq"), dk.check("dk"), dv.check("dv")
     return o.t, lse.t, dq.t, dk.t, dv.t
+
+
+def _same_bits(a, b, what):
+    import torch
+    assert torch.equal(a, b), f"{what}: the two backward forms differ"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -271,7 +277,13 @@ def test_attention_fwd_bwd(dtype, B, L, hq, hkv, dh):
     k = _rand(rng, (B, L, hkv, dh), 1.0, dtype)
     v = _rand(rng, (B, L, hkv, dh), 1.0, dtype)
     do = _rand(rng, (B, L, hq, dh), 1.0, dtype)
-    _attn_check(dtype, q, k, v, do, *_attn_run(dtype, q, k, v, do))
+    res = _attn_run(dtype, q, k, v, do)
+    _attn_check(dtype, q, k, v, do, *res)
+    if dtype == "bf16":
+        # dQ from the stored dS and dQ from a recomputation: the same bits.
+        alt = _attn_run(dtype, q, k, v, do, stored_ds=False)
+        for name, a, b in zip(("dq", "dk", "dv"), res[2:], alt[2:]):
+            _same_bits(a, b, name)
 
 
 def test_attention_strided_views():
