@@ -152,6 +152,13 @@ __device__ inline void lds_dma16_r(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(r), "s"(soff), "s"(lds_base) : "memory", "m0");
 }
+// The same with the non-temporal policy: for data read once (it streams
+// through the caches instead of displacing what other waves re-read).
+__device__ inline void lds_dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                   uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+               :: "v"(voff), "s"(r), "s"(soff), "s"(lds_base) : "memory", "m0");
+}
 __device__ inline void lds_dma16(uint64_t p, uint32_t voff, uint32_t soff, uint32_t lds_base) {
   lds_dma16_r(__builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, 0x7FFFFFFF, 0x00020000),
               voff, soff, lds_base);
