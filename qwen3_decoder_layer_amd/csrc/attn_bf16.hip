@@ -16,15 +16,17 @@
 //   accumulators.  Output: O (bf16) and the log-sum-exp per query (fp32).
 //
 // Backward (P recomputed from the saved log-sum-exp):
-//   delta = rowsum(dO * O) per query, formed by the dQ kernel from the dO
-//     rows it holds anyway (so it runs first);
+//   delta = rowsum(dO * O) per query, by a row-sum kernel that runs first;
 //   dK/dV kernel: a workgroup owns 128 keys of one kv head (32 per wave; K
 //     and V in LDS) and sweeps every q head of the group and every query
 //     tile at or after its keys (Q / dO tiles and their LSE / delta by
 //     direct loads, transposed operands by transposing reads); dK^T and
 //     dV^T accumulate in registers, so the G-head sum (adjoint of
-//     repeat_interleave) needs no atomics;
-//   dQ kernel: the forward's shape, accumulating dQ^T over key tiles.
+//     repeat_interleave) needs no atomics.  In the stored-dS form it also
+//     writes dS = P (dP - delta) (bf16) to a scratch buffer;
+//   dQ: from that dS (dQ^T += K^T dS^T, one product), or, in the
+//     recomputing form, by a kernel of the forward's shape that recomputes
+//     S and dP per key tile.  Both forms give the same bits.
 #include <climits>
 #include <type_traits>
 
@@ -58,7 +60,7 @@ struct FwdP {
   // backward
   const bf16_t* dout; int64_t lddo;
   bf16_t* dq; bf16_t* dk; bf16_t* dv;
-  float* delta;   // written by the dQ (or row-sum) kernel, read by dK/dV
+  float* delta;   // written by the row-sum kernel, read by the others
   // stored-dS form: the dS blocks of the causal triangle (bf16), ds_nt
   // blocks per (sequence, q head); null for the recomputing form.
   bf16_t* ds; int64_t ds_nt;
@@ -902,26 +904,10 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dqt[dt][e] = 0.f;
 
-  // D = rowsum(dO * O) of this lane's row: the dO fragments are already in
-  // registers (elements 16 kk + 8h .. +7), O's same elements are loaded, and
-  // the two halves of the row meet across the lane halves.  The dK/dV
-  // kernel, launched after this one, reads D back.  The first K/V tile is
-  // requested between the loads of O and their use, so it overlaps this.
-  float dlt = 0.f;
-  {
-    const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
-    u32x4_t ov[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) ov[kk] = ld16(opo + 16 * kk);
-    load_tile(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
-    dlt += __shfl_xor(dlt, 32, 64);
-    if (h == 0 && qrow < L) p.delta[sidx] = dlt;
-  }
+  // D = rowsum(dO * O) of this lane's row, from the row-sum kernel (launched
+  // before this one); the first K/V tile is requested before it is read.
+  load_tile(0, 0);
+  const float dlt = p.delta[sidx];
 
   wait_vmcnt<0>();
   stage_barrier();
@@ -1022,37 +1008,41 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
     }
 }
 
-// Row sums D = rowsum(dO * O) for the stored-dS form, where no dQ kernel
-// runs before dK/dV: one wave per 32 rows of one q head, each lane half
-// summing half of a row in the order the dQ kernel above uses (so both forms
-// read the same D).
+// Row sums D = rowsum(dO * O) (fp32) per (sequence, q head, query), read by
+// both dQ kernels and by dK/dV.  A workgroup takes 4 passes of 256 / (d_h / 8)
+// rows of one q head: each lane loads 16 bytes of dO and of O (a pass reads
+// whole rows, contiguous), multiplies in fp32, and the d_h / 8 lanes of a row
+// sum their partials by lane exchanges.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p) {
-  constexpr int NKK = DH / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
+  constexpr int LPR = DH / 8;                  // lanes per row
+  constexpr int RPP = 256 / LPR;               // rows per pass
+  constexpr int NP = 4;                        // passes
+  const int t = threadIdx.x, c = t % LPR;
   const int b = blockIdx.x / p.h_q, head = blockIdx.x % p.h_q;
   const int L = p.L;
-  const int qw0 = blockIdx.y * 128 + 32 * wave;
-  if (qw0 >= L) return;
-  const int qrow = qw0 + l32, qr = min(qrow, L - 1);
   const int64_t tok0 = (int64_t)b * L;
-  const bf16_t* op = p.dout + (tok0 + qr) * p.lddo + (int64_t)head * DH + 8 * h;
-  const bf16_t* opo = p.o + (tok0 + qr) * p.ldo + (int64_t)head * DH + 8 * h;
-  u32x4_t of[NKK], ov[NKK];
+  u32x4_t of[NP], ov[NP];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    of[kk] = ld16(op + 16 * kk);
-    ov[kk] = ld16(opo + 16 * kk);
+  for (int i = 0; i < NP; ++i) {
+    const int q = (blockIdx.y * NP + i) * RPP + t / LPR;
+    of[i] = ov[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (q < L) {
+      of[i] = ld16(p.dout + (tok0 + q) * p.lddo + (int64_t)head * DH + 8 * c);
+      ov[i] = ld16(p.o + (tok0 + q) * p.ldo + (int64_t)head * DH + 8 * c);
+    }
   }
-  float dlt = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
+  for (int i = 0; i < NP; ++i) {
+    float d = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      dlt += lo_f(of[kk][w]) * lo_f(ov[kk][w]) + hi_f(of[kk][w]) * hi_f(ov[kk][w]);
-  dlt += __shfl_xor(dlt, 32, 64);
-  if (h == 0 && qrow < L) p.delta[((int64_t)b * p.h_q + head) * L + qrow] = dlt;
+      d += lo_f(of[i][w]) * lo_f(ov[i][w]) + hi_f(of[i][w]) * hi_f(ov[i][w]);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) d += __shfl_xor(d, m, 64);
+    const int q = (blockIdx.y * NP + i) * RPP + t / LPR;
+    if (c == 0 && q < L) p.delta[((int64_t)b * p.h_q + head) * L + q] = d;
+  }
 }
 
 // dQ from the stored dS: dQ^T += K^T dS^T over the key blocks at or before
@@ -1249,26 +1239,28 @@ hipError_t attn_bwd_bf16(const AttnArgs& a, hipStream_t s) {
   dim3 kgrid((unsigned)(p.B * p.h_kv), (unsigned)cdiv(p.L, 128));
   const int QB = 32 * p.rb;
   dim3 qgrid((unsigned)(p.B * p.h_kv * (p.G / p.hb)), (unsigned)cdiv(p.L, QB));
+  // The row sums D first (both forms read them).
+  if (a.d_h == 128)
+    hipLaunchKernelGGL(attn_delta_kernel<128>, dim3((unsigned)(p.B * p.h_q), (unsigned)cdiv(p.L, 64)),
+                       dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(attn_delta_kernel<64>, dim3((unsigned)(p.B * p.h_q), (unsigned)cdiv(p.L, 128)),
+                       dim3(256), 0, s, p);
   if (p.ds) {
-    // Stored dS: the row sums D, then dK/dV (which also writes dS), then dQ
-    // from dS.
-    dim3 dgrid((unsigned)(p.B * p.h_q), (unsigned)cdiv(p.L, 128));
+    // Stored dS: dK/dV (which also writes dS), then dQ from dS.
     dim3 dsgrid(qgrid.x, (unsigned)cdiv(p.L, 64 * (kDqWaves / p.hb)));
     if (a.d_h == 128) {
-      hipLaunchKernelGGL(attn_delta_kernel<128>, dgrid, dim3(256), 0, s, p);
       hipLaunchKernelGGL((attn_dkdv_kernel<128, true>), kgrid, dim3(512), 0, s, p);
       hipLaunchKernelGGL((attn_dq_ds_kernel<128, kDqWaves, kDqStages>), dsgrid,
                          dim3(64 * kDqWaves), 0, s, p);
     } else {
-      hipLaunchKernelGGL(attn_delta_kernel<64>, dgrid, dim3(256), 0, s, p);
       hipLaunchKernelGGL((attn_dkdv_kernel<64, true>), kgrid, dim3(512), 0, s, p);
       hipLaunchKernelGGL((attn_dq_ds_kernel<64, kDqWaves, kDqStages>), dsgrid,
                          dim3(64 * kDqWaves), 0, s, p);
     }
     return hipGetLastError();
   }
-  // Recomputing form.  dQ first: it also writes the row sums D that dK/dV
-  // reads.
+  // Recomputing form: dQ (recomputing S and dP), then dK/dV.
   if (a.d_h == 128) {
     hipLaunchKernelGGL(attn_dq_kernel<128>, qgrid, dim3(256), 0, s, p);
     hipLaunchKernelGGL((attn_dkdv_kernel<128, false>), kgrid, dim3(512), 0, s, p);
