@@ -43,10 +43,9 @@ COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 # --kernel-probe`, each scaled by what the same counter reads for the 1 GiB
 # calibration copy.  Valid only for the kernel source it was taken on: the
 # digest below is of gemm_bf16.hip, and a changed source reports null.
-TRAFFIC = {"source_sha256": "308dc6e7f6ecf8b2",
-           "fetch_kib": 1181332.7, "write_kib": 592372.0,
-           "copy_fetch_kib": 524303.0, "copy_write_kib": 1048576.0,
-           "bytes": 3025889103}
+TRAFFIC = {"source_sha256": "52c84c34524a98f3",
+           "fetch_kib": 1181001.7, "write_kib": 592221.6, "copy_fetch_kib": 524303.0,
+           "copy_write_kib": 1048576.0, "bytes": 3025057346}
 
 WORKLOADS = {
     "qwen3-8b-bf16-fwd-bwd": 4,
