@@ -82,6 +82,14 @@ __device__ inline u32x4_t pack_half(const f32x16_t& s, int half) {
 // small) flush to zero instead of taking the library's denormal-scaling path.
 __device__ inline float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global->LDS load of 4 bytes per lane through a buffer resource
+// (lane i's dword lands at LDS byte lds_base + 4 i; offsets past the
+// resource's range read zeros), written like the 16-byte form in common.h.
+__device__ inline void lds_dma4_r(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "s"(lds_base) : "memory", "m0");
+}
+
 // LDS row layout of the K/V/Q/dO tiles: a [rows][d_h] bf16 tile
 // stored row-major with its 16-byte chunks permuted per row: chunk c of row
 // r sits at slot c ^ swz(r).  The LDS serves 256 bytes (64 banks of 4) per
@@ -614,17 +622,18 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   TileLoader<DH, QT, 8> qld, old_;
   qld.init(p.ldq, wave, lane);
   old_.init(p.lddo, wave, lane);
-  auto load_tile = [&](int it, int s) {
-    const int head = kvh * p.G + it / nqt;
-    const int q0 = (qt_first + it % nqt) * QT;
+  // Tile (head index hi of the group, query tile qi of the nqt): the tile
+  // counters advance incrementally (no division per tile).
+  auto load_tile = [&](int hi, int qi, int s) {
+    const int head = kvh * p.G + hi;
+    const int q0 = (qt_first + qi) * QT;
     qld.load(p.q, p.ldq, tok0, head * DH, q0, L, stage(s), wave);
     old_.load(p.dout, p.lddo, tok0, head * DH, q0, L, stage(s) + TB, wave);
     if (wave < 2) {   // log-sum-exp (wave 0) and row sums (wave 1), 64 floats each
-      const float* src = wave == 0 ? (const float*)p.lse : p.delta;
-      const int q = q0 + lane;
-      const uint32_t off =
-          q < L ? (uint32_t)((((int64_t)b * p.h_q + head) * L + q) * 4) : kOOB;
-      lds_dma4((uint64_t)src, off, uni(lds_addr(ldsLD + (2 * s + wave) * QT)));
+      const float* src = (wave == 0 ? (const float*)p.lse : p.delta) +
+                         ((int64_t)b * p.h_q + head) * L + q0;
+      lds_dma4_r(buf_rsrc(src, (uint32_t)(L - q0) * 4u), 4u * (uint32_t)lane,
+                 uni(lds_addr(ldsLD + (2 * s + wave) * QT)));
     }
   };
 
@@ -635,7 +644,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
     kl.load(p.k, p.ldk, tok0, kvh * DH, kb0, L, sK, wave);
     vl.load(p.v, p.ldv, tok0, kvh * DH, kb0, L, sV, wave);
   }
-  load_tile(0, 0);
+  load_tile(0, 0, 0);
   wait_vmcnt<0>();
   stage_barrier();
 
@@ -663,14 +672,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
   // Stored-dS form: the lane's byte offset inside a block (see above).
   const uint32_t ds_off = 256u * (uint32_t)(l32 >> 2) + 64u * (uint32_t)h + 16u * (uint32_t)(l32 & 3);
 
+  int hcur = 0, qcur = 0;   // the tile of iteration it
   for (int it = 0; it < total; ++it) {
     const int s = it & 1;
-    if (it + 1 < total) load_tile(it + 1, s ^ 1);
-    const int qh0 = (qt_first + it % nqt) * QT + 32 * half;   // this wave's first row
+    const int qnx = qcur + 1 == nqt ? 0 : qcur + 1;
+    const int hnx = qcur + 1 == nqt ? hcur + 1 : hcur;
+    if (it + 1 < total) load_tile(hnx, qnx, s ^ 1);
+    const int qh0 = (qt_first + qcur) * QT + 32 * half;   // this wave's first row
     __amdgpu_buffer_rsrc_t rds = buf_rsrc(nullptr, 0);
     if constexpr (DS) {
       // This block's 2 KB (none for rows past the sequence: stores dropped).
-      const int head = kvh * p.G + it / nqt;
+      const int head = kvh * p.G + hcur;
       const int64_t qb = qh0 / 32, kb = kw0 / 32;
       const int64_t blk = (qb * (qb + 1) / 2 + kb) * (p.B * p.h_q) + (int64_t)b * p.h_q + head;
       rds = buf_rsrc(p.ds + blk * 1024, qh0 < L ? 2048u : 0u);
@@ -797,6 +809,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
       block((qh0 < kw0 + 31) || (qh0 + 32 > L) || (kw0 + 32 > L));
     wait_vmcnt<0>();      // this wave's part of tile it+1 has landed
     stage_barrier();      // everyone's part; stage s fully read
+    hcur = hnx;
+    qcur = qnx;
   }
 
   // Waves 4..7 hand their partial sums to waves 0..3 through LDS (the

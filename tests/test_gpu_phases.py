@@ -286,6 +286,33 @@ def test_attention_fwd_bwd(dtype, B, L, hq, hkv, dh):
             _same_bits(a, b, name)
 
 
+def test_attention_backward_forms_full_size():
+    """The Qwen3-8B attention shape in full (B=2, L=4096, 32 q heads on 8 kv
+    heads, d_h=128, inside the layer's [T, q|k|v] buffer): dQ from the stored
+    dS and dQ from a recomputation of S and dP, every element of dq, dk and
+    dv bitwise equal (the layer tests compare these shapes with the oracle
+    on sampled rows)."""
+    need_gpu()
+    import torch
+    say("attention backward forms, B=2 L=4096 hq=32 hkv=8 dh=128")
+    B, L, hq, hkv, dh = 2, 4096, 32, 8, 128
+    qd, kvd = hq * dh, hkv * dh
+    g = torch.Generator(device="cuda").manual_seed(4096)
+    qkv = torch.randn(B, L, qd + 2 * kvd, device="cuda", generator=g).to(torch.bfloat16)
+    do = torch.randn(B, L, qd, device="cuda", generator=g).to(torch.bfloat16)
+    gq, gk, gv = qkv[..., :qd], qkv[..., qd:qd + kvd], qkv[..., qd + kvd:]
+    o, lse = q3.attention_fwd(gq, gk, gv, hq, hkv, dh)
+    outs = []
+    for stored in (True, False):
+        grad = torch.full_like(qkv, float("nan"))
+        q3.attention_bwd(gq, gk, gv, o, do, lse, hq, hkv, dh, dq=grad[..., :qd],
+                         dk=grad[..., qd:qd + kvd], dv=grad[..., qd + kvd:], stored_ds=stored)
+        outs.append(grad)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0].float()).all())
+    _same_bits(outs[0], outs[1], "dq|dk|dv")
+
+
 def test_attention_strided_views():
     """q/k/v read from column slices of one [T, q+k+v] buffer (the layer's
     layout), forward and backward; dq/dk/dv are written with the same row
