@@ -177,7 +177,10 @@ size_t q3l_saved_bytes(const q3l_layer_cfg *cfg);
 
 /* Bytes of scratch workspace: backward == 0 for q3l_layer_forward (this
  * includes room for the intermediates when `saved` is NULL), backward == 1
- * for q3l_layer_backward.  0 if cfg is invalid. */
+ * for q3l_layer_backward.  0 if cfg is invalid.  The bf16 backward's includes
+ * the attention backward's dS (see q3l_attention_bwd) while that stays
+ * within 8 GiB (about B h_q L^2 bytes; 1.08 GB at B = 2, L = 4096, 32 q
+ * heads); beyond, the attention backward recomputes S and dP for dQ. */
 size_t q3l_workspace_bytes(const q3l_layer_cfg *cfg, int backward);
 
 /* Forward of the layer (walkthrough page, Steps 1-10).

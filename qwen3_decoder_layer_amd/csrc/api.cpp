@@ -139,6 +139,9 @@ q3l_saved_layout saved_layout(const q3l_layer_cfg& c) {
   return s;
 }
 
+constexpr size_t kStoredDsMax = size_t(8) << 30;   // the stored-dS workspace cap
+constexpr size_t kNone = ~size_t(0);                // no such region
+
 struct BwdWs {
   // wpart_post / wpart_in: partial-row sums of the two RMSNorm weight
   // gradients (separate, so an input-gradient-only call leaves both for the
@@ -174,7 +177,10 @@ BwdWs bwd_layout(const q3l_layer_cfg& c) {
     const size_t Tp = (size_t)pad8(m.T);
     w.tA = take((size_t)std::max<int64_t>(std::max<int64_t>(2LL * m.ffn, m.nqkv), m.d) * Tp * 2);
     w.tC = take((size_t)m.d * Tp * 2);
-    w.ds = take(attn_ds_bytes(m.B, m.L, m.hq));
+    // dS for the attention backward while it stays within kStoredDsMax
+    // (about B h_q L^2 bytes; beyond, the backward recomputes S and dP for dQ).
+    w.ds = attn_ds_bytes(m.B, m.L, m.hq) <= kStoredDsMax ? take(attn_ds_bytes(m.B, m.L, m.hq))
+                                                         : kNone;
   }
   w.total = off;
   return w;
@@ -758,7 +764,7 @@ q3l_status q3l_layer_backward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     a.dq = dqk; a.dk = dqk + (size_t)m.qd * m.es;
     a.dv = dqkv + (size_t)(m.qd + m.kvd) * m.es;
     a.delta = delta;
-    a.ds = bt ? at(workspace, W.ds) : nullptr;
+    a.ds = (bt && W.ds != kNone) ? at(workspace, W.ds) : nullptr;
     Q3L_HIP(attn_bwd(dt, a, s));
   }
   Q3L_HIP(mk.end(11));

@@ -137,6 +137,25 @@ def test_workspace_grows_with_backward(abi, lib):
         lib.q3l_workspace_bytes(C.byref(cfg), 0)
 
 
+def test_backward_workspace_holds_ds_up_to_its_cap(abi, lib):
+    # The bf16 layer backward's workspace holds the attention backward's dS
+    # (B h_q n(n+1)/2 blocks of 2 KB, n = ceil(L/32)) while that is at most
+    # 8 GiB; past it the backward recomputes and the region is left out.
+    def ws(L, dtype=abi.Q3L_BF16):
+        cfg = cfg_of(abi, d=4096, h_q=32, h_kv=8, d_h=128, d_ffn=12288, B=2, L=L, dtype=dtype)
+        return lib.q3l_workspace_bytes(C.byref(cfg), 1)
+    def ds(L):
+        n = (L + 31) // 32
+        return 2 * 32 * n * (n + 1) // 2 * 2048
+    assert ds(8192) < 8 << 30 < ds(16384)
+    # Every other region is affine in L (a fixed part for the norm-weight
+    # partial sums): the 16384-token workspace is what the line through the
+    # 4096- and 8192-token sizes without dS predicts.
+    lin = lambda L: ws(L) - ds(L)
+    assert abs(ws(16384) - (lin(8192) + 2 * (lin(8192) - lin(4096)))) < 1 << 20
+    assert ws(4096, abi.Q3L_F32) < ws(4096)
+
+
 def test_forward_rejects_null_and_misaligned_pointers_before_launch(abi, lib):
     cfg = cfg_of(abi)
     buf = C.create_string_buffer(4096)
