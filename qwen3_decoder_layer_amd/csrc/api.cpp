@@ -1191,7 +1191,7 @@ q3l_status q3l_attention_bwd(int32_t dtype, int32_t B, int32_t L, int32_t h_q, i
 // on holds its own copy until the process ends.  Host code uses the array's
 // device address, taken once per device with hipGetSymbolAddress (the
 // array's name on the host is only a stand-in).  Nothing in it has to start
-// at zero: the dQ kernel writes every row sum the dK/dV kernel then reads.
+// at zero: the row-sum kernel writes every row sum the later kernels read.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr size_t kScratchFloats = size_t(1) << 22;   // 16 MiB: B*h_q*L <= 4M
