@@ -40,14 +40,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int KT = 64;        // keys per tile
 constexpr float kTau = 8.0f;  // rescale threshold (log2 units), see the forward
-#ifndef Q3L_DQ_STAGES
-#define Q3L_DQ_STAGES 3
-#endif
-constexpr int kDqStages = Q3L_DQ_STAGES;   // LDS stages of the dQ-from-dS kernel
-#ifndef Q3L_DQ_WAVES
-#define Q3L_DQ_WAVES 8
-#endif
-constexpr int kDqWaves = Q3L_DQ_WAVES;     // its waves per workgroup
+// The dQ-from-dS kernel: LDS stages and waves per workgroup (measured: 3
+// stages beat 2 by 3%, 4 gain nothing; 8 waves beat 4).
+constexpr int kDqStages = 3;
+constexpr int kDqWaves = 8;
 
 struct FwdP {
   int B, L, h_q, h_kv, G, hb, rb;
