@@ -145,8 +145,10 @@ typedef struct {
    * set, fork_event and join_event must be hipEvent_t the caller created
    * (timing may be disabled).  The call records fork_event on `stream`,
    * makes side_stream wait for it, enqueues the copy on side_stream,
-   * records join_event there and makes `stream` wait for it: all work of the
-   * call stays ordered on `stream` (and can be captured into a HIP graph).
+   * records join_event there and, at the end of the forward (after the last
+   * phase mark, and on every error path once the join event is recorded),
+   * makes `stream` wait for it: all work of the call stays ordered on
+   * `stream` (and can be captured into a HIP graph).
    * Calls that share these objects must not be made concurrently. */
   void *side_stream;
   void *fork_event;

@@ -295,6 +295,20 @@ const char* const kBwdPhases[] = {
 constexpr int kNumFwdPhases = sizeof(kFwdPhases) / sizeof(kFwdPhases[0]);
 constexpr int kNumBwdPhases = sizeof(kBwdPhases) / sizeof(kBwdPhases[0]);
 
+// Orders the caller's stream after work forked to its second stream: on
+// the way out of the call, whatever path it takes, the caller's stream waits
+// for the join event (join() does it early and reports the status).
+struct Join {
+  hipStream_t s = nullptr;
+  hipEvent_t ev = nullptr;
+  hipError_t join() {
+    const hipError_t e = ev ? hipStreamWaitEvent(s, ev, 0) : hipSuccess;
+    ev = nullptr;
+    return e;
+  }
+  ~Join() { (void)join(); }
+};
+
 struct Marks {
   void* const* ev = nullptr;
   int next = 0;
@@ -415,6 +429,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
   mk.s = s;
   mk.ev = exec ? exec->marks : nullptr;
   hipStream_t side = (copies && exec) ? static_cast<hipStream_t>(exec->side_stream) : nullptr;
+  Join joiner;
   float* rstd1 = reinterpret_cast<float*>(at(S, L.rstd1));
   void* xn = at(S, L.xn);
   void* qkv = at(S, L.qkv);
@@ -472,14 +487,14 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
       Q3L_HIP(hipStreamWaitEvent(side, fork, 0));
       const hipError_t e1 = transposed_copies(c, xn, at(S, L.xnt), side);
       const hipError_t e2 = hipEventRecord(join, side);
+      // The caller's stream waits for the join at the end of the forward
+      // (on any path out of it: `joiner`), not here, so the attention's
+      // phase holds no cross-stream wait.
+      if (e2 == hipSuccess) { joiner.s = s; joiner.ev = join; }
       const hipError_t e3 = attn_fwd(dt, a, s);
-      // Joined whatever happened above, so nothing of this call is left
-      // running unordered with the caller's stream.
-      const hipError_t e4 = hipStreamWaitEvent(s, join, 0);
       Q3L_HIP(e1);
       Q3L_HIP(e2);
       Q3L_HIP(e3);
-      Q3L_HIP(e4);
     } else {
       Q3L_HIP(attn_fwd(dt, a, s));
     }
@@ -523,6 +538,7 @@ q3l_status q3l_layer_forward(const q3l_layer_cfg* cfg, const q3l_weights* w,
     Q3L_HIP(gemm(dt, g, s));
   }
   Q3L_HIP(mk.end(8));
+  Q3L_HIP(joiner.join());
   g_err.clear();
   return Q3L_OK;
 }
