@@ -1064,9 +1064,11 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const FwdP p) {
 // blocks (zeros for a block past the diagonal or the sequence end: its
 // products then add nothing), NST stages deep, all by direct global->LDS
 // loads; dS, read once, with the non-temporal policy (11% faster: the K
-// tiles that other workgroups re-read stay in the L2).  The accumulation order is the recomputing dQ kernel's (d block by
-// d block, 16-key steps in key order, the same transposed K fragments), so
-// both forms give the same bits.  The dS^T operand (lane = query, eight
+// tiles that other workgroups re-read stay in the L2).  The accumulation
+// order is the recomputing dQ kernel's (d block by d block, 16-key steps in
+// key order, the same transposed K fragments), so both forms give the same
+// bits.  The kernel is bound by its loads (alone they take 197 of its
+// 201 us; the products alone 155).  The dS^T operand (lane = query, eight
 // keys) comes from transposing reads of a block as the dK/dV kernel stored
 // it: for 16-key step ks, source lane sl of 16-lane group g reads keys
 // 16 ks + 4 (g / 2) + sl / 4 (+8 for the second read), queries
