@@ -431,6 +431,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
       float rs = 0.f;
       u32x4_t pf[4];
       // ---- A: scores of tile t+1, exponentials of tile t ----
+      // The wave runs phase A at raised priority: where the other wave on
+      // its SIMD (another workgroup, not in step with it) is in phase B, A's
+      // instructions go first (1.8% faster than equal priorities).
+      __builtin_amdgcn_s_setprio(1);
       {
         auto kfrag = [&](int j) __attribute__((always_inline)) {
           return ld_lds16((const Q3L_LDS void*)(uintptr_t)(
@@ -499,6 +503,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdP p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       };
+      __builtin_amdgcn_s_setprio(0);
       phase_b(std::true_type{});
       if (more && edge_tile(kv1)) {
         mx = -INFINITY;
