@@ -286,16 +286,21 @@ def test_attention_fwd_bwd(dtype, B, L, hq, hkv, dh):
             _same_bits(a, b, name)
 
 
-def test_attention_backward_forms_full_size():
+@pytest.mark.parametrize("B,L", [(2, 4096), (1, 11586)], ids=["qwen3-8b", "ds-past-4GiB"])
+def test_attention_backward_forms_full_size(B, L):
     """The Qwen3-8B attention shape in full (B=2, L=4096, 32 q heads on 8 kv
-    heads, d_h=128, inside the layer's [T, q|k|v] buffer): dQ from the stored
-    dS and dQ from a recomputation of S and dP, every element of dq, dk and
-    dv bitwise equal (the layer tests compare these shapes with the oracle
-    on sampled rows)."""
+    heads, d_h=128, inside the layer's [T, q|k|v] buffer), and one sequence
+    long enough that the stored dS passes 4 GiB (32-bit byte offsets would
+    wrap): dQ from the stored dS and dQ from a recomputation of S and dP,
+    every element of dq, dk and dv bitwise equal (the layer tests compare
+    the first shape with the oracle on sampled rows)."""
     need_gpu()
     import torch
-    say("attention backward forms, B=2 L=4096 hq=32 hkv=8 dh=128")
-    B, L, hq, hkv, dh = 2, 4096, 32, 8, 128
+    hq, hkv, dh = 32, 8, 128
+    say(f"attention backward forms, B={B} L={L} hq={hq} hkv={hkv} dh={dh}")
+    n = (L + 31) // 32
+    if L > 4096:
+        assert B * hq * n * (n + 1) // 2 * 2048 > 4 << 30
     qd, kvd = hq * dh, hkv * dh
     g = torch.Generator(device="cuda").manual_seed(4096)
     qkv = torch.randn(B, L, qd + 2 * kvd, device="cuda", generator=g).to(torch.bfloat16)
