@@ -65,8 +65,6 @@ struct FwdP {
   float* m_out; float* l_out; float* acc; int64_t ld_acc;
 };
 
-__device__ inline u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
-
 // Pack accumulator values i = 8*half .. 8*half+7 (bf16) into a k-operand.
 __device__ inline u32x4_t pack_half(const f32x16_t& s, int half) {
   const int b = 8 * half;
@@ -704,7 +702,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(const FwdP p) {
     // registers than there are).
     auto block = [&](bool edge) __attribute__((always_inline)) {
       const Q3L_LDS char* sQ = stage(s);
-      const Q3L_LDS char* sO = sQ + TB;
       f32x16_t sc, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sc[e] = 0.f; dp[e] = 0.f; }
@@ -931,7 +928,6 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(const FwdP p) {
     if (t + 1 < ntiles) load_tile(t + 1, s ^ 1);
     if (t < my_tiles) {
       const Q3L_LDS char* sK = stage(s);
-      const Q3L_LDS char* sV = sK + TB;
       const int kv0 = t * KT;
       f32x16_t sc[2], dp[2];
 #pragma unroll
